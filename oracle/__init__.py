@@ -1,0 +1,15 @@
+"""fp64 CPU oracle for batched draft verification — test infrastructure only.
+
+Imported by the tests, the smoke check and the benchmark's CPU-baseline leg; never by the GPU
+library.
+"""
+from .sv_oracle import (AMBIGUOUS_MARGIN, BatchResult, RequestResult, accept_threshold,
+                        argmax_lowest, decode_logits, inverse_cdf, residual_weights,
+                        softmax_fp64, verify_batch, verify_greedy, verify_greedy_request,
+                        verify_request)
+
+__all__ = [
+    "AMBIGUOUS_MARGIN", "BatchResult", "RequestResult", "accept_threshold", "argmax_lowest",
+    "decode_logits", "inverse_cdf", "residual_weights", "softmax_fp64", "verify_batch",
+    "verify_greedy", "verify_greedy_request", "verify_request",
+]

@@ -1,0 +1,229 @@
+"""Seeded synthetic inputs for batched draft verification.
+
+This module only draws random inputs: target and draft logits, draft tokens, per-slot
+uniforms, the residual uniform and the per-request number of drafts to verify. It holds none
+of the verification arithmetic (no softmax, no acceptance test, no residual sampling), so that
+the oracle and the GPU path can both consume its output without sharing any of the method.
+
+Draft tokens for sampling workloads are drawn from softmax(d / tau) with the exponential-race
+form of the Gumbel-max construction: x = argmax_v (d_v / tau - log E_v), E_v ~ Exp(1) i.i.d.
+Since -log E_v is standard Gumbel, x has exactly the categorical law softmax(d / tau) of the
+stored (already rounded) draft row. Greedy workloads take x = argmax_v d_v (lowest index on
+ties), the proposal a greedy drafter makes.
+
+Shapes and value distributions stand in for the pages' workloads (no dataset is used):
+  * vocabulary 151936, the size of the Qwen3-8B target used for the single-H100 comparison in
+    "From draft-then-verify to DSpark" and for the vLLM demo in the DSpark paper review;
+  * draft blocks of 4-16 tokens ("Accelerating Large-Model Inference ...", section 4 setup;
+    block_size 8 in its section 8 config table; 7 speculative tokens in the DSpark review);
+  * one request in flight vs 64 in flight vs a heavily loaded batch (DSpark review, section 6);
+  * per-request verify lengths that differ inside one batch (DSpark review, 4.2.2 and 5.3);
+  * later draft slots agreeing less with the target ("suffix decay", DSpark review 3.2 and
+    "From draft-then-verify to DSpark", DFlash section).
+
+Randomness: every request b of a workload draws from its own generator
+numpy.random.default_rng(SeedSequence([seed, b])), in this fixed order:
+  1. target normals [K+1, V] (float32);  2. spike indices [K+1] (if the workload has a spike);
+  3. draft noise [K, V] (float32);       4. draft-token exponentials [K, V] (sampling only);
+  5. per-slot uniforms u [K] (float32);  6. residual uniform r (float32);
+  7. the number of drafts k_b (ragged workloads only).
+Noise is added in float32; bf16 storage rounds to nearest, ties to even.
+"""
+from __future__ import annotations
+
+import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Optional, Sequence
+
+import numpy as np
+
+QWEN3_VOCAB = 151936
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """A seeded synthetic verify workload (one batch of B requests)."""
+
+    name: str
+    B: int
+    K: int
+    V: int
+    dtype: str  # "f32" or "bf16": storage type of both logit tensors
+    temperature: float
+    mode: str  # "sample" or "greedy"
+    target_sigma: float
+    spike: float  # added to one random vocabulary entry per target row; 0 = none
+    draft_sigma: Sequence[float]  # per draft slot, length K
+    identical_even: bool = False  # even requests: draft rows = target rows bitwise
+    ragged: bool = False  # k_b ~ U{1..K}; rows past k_b are NaN-filled
+    seed: int = 0
+
+    @property
+    def rows_per_request(self) -> int:
+        return 2 * self.K + 1 if self.mode == "sample" else self.K + 1
+
+    def replace(self, **kw) -> "Workload":
+        if "K" in kw and "draft_sigma" not in kw:
+            s = self.draft_sigma
+            if len(set(s)) == 1:
+                kw["draft_sigma"] = (s[0],) * kw["K"]
+            else:  # keep the linear ramp shape from first to last slot
+                k = kw["K"]
+                kw["draft_sigma"] = tuple(
+                    s[0] + (s[-1] - s[0]) * (i / (k - 1) if k > 1 else 0.0) for i in range(k)
+                )
+        return dataclasses.replace(self, **kw)
+
+
+def _ramp(lo: float, hi: float, k: int) -> tuple:
+    return tuple(lo + (hi - lo) * i / (k - 1) for i in range(k)) if k > 1 else (lo,)
+
+
+# The five workloads: tiny correctness case, interactive, batched (the throughput headline),
+# heavy ragged load, and greedy mode.
+TINY = Workload("tiny_sample_B1_K4_V1000_f32", 1, 4, 1000, "f32", 1.0, "sample",
+                2.0, 0.0, (0.5,) * 4, seed=1001)
+INTERACTIVE = Workload("interactive_sample_B1_K8_V151936_f32", 1, 8, QWEN3_VOCAB, "f32", 1.0,
+                       "sample", 3.0, 12.0, (1.0,) * 8, seed=1002)
+BATCHED = Workload("batched_sample_B64_K8_V151936_bf16_t0.7", 64, 8, QWEN3_VOCAB, "bf16", 0.7,
+                   "sample", 3.0, 12.0, (1.5,) * 8, identical_even=True, seed=1003)
+HEAVY = Workload("heavy_ragged_sample_B256_K16_V151936_bf16", 256, 16, QWEN3_VOCAB, "bf16",
+                 1.0, "sample", 3.0, 12.0, _ramp(0.5, 3.0, 16), ragged=True, seed=1004)
+GREEDY = Workload("greedy_B512_K8_V151936_f32", 512, 8, QWEN3_VOCAB, "f32", 1.0, "greedy",
+                  3.0, 12.0, (1.0,) * 8, seed=1005)
+
+WORKLOADS = {w.name: w for w in (TINY, INTERACTIVE, BATCHED, HEAVY, GREEDY)}
+BY_NUMBER = {1: TINY, 2: INTERACTIVE, 3: BATCHED, 4: HEAVY, 5: GREEDY}
+
+
+def sweep_workload(K: int, B: int, dtype: str, mode: str = "sample") -> Workload:
+    """K x B sweep point: batched-workload distributions, temperature 1."""
+    return BATCHED.replace(name=f"sweep_{mode}_B{B}_K{K}_V{QWEN3_VOCAB}_{dtype}", K=K, B=B,
+                           dtype=dtype, temperature=1.0, mode=mode,
+                           draft_sigma=(1.5,) * K, seed=2000 + 100 * K + B)
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), round to nearest, ties to even.
+
+    Finite inputs only (the generator never rounds a NaN or an infinity)."""
+    bits = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((bits >> np.uint32(16)) & np.uint32(1))
+    return ((bits + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float32 values (exact widening)."""
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32)
+            << np.uint32(16)).view(np.float32)
+
+
+BF16_NAN = np.uint16(0x7FC0)
+
+
+@dataclasses.dataclass
+class Inputs:
+    """Host arrays of one workload.
+
+    target: [B, K+1, V] float32 or uint16 (bf16 bits); draft: [B, K, V] same type, or None for
+    greedy workloads (draft logits are only used on the host to choose the proposals).
+    tokens [B, K] int32; uniforms [B, K] float32; residual [B] float32;
+    num_draft [B] int32 (None when every request verifies all K drafts).
+    Masked slots (s >= k_b) hold token -1, uniform NaN and NaN logit rows.
+    """
+
+    workload: Workload
+    target: np.ndarray
+    draft: Optional[np.ndarray]
+    tokens: np.ndarray
+    uniforms: np.ndarray
+    residual: np.ndarray
+    num_draft: Optional[np.ndarray]
+
+    @property
+    def B(self):
+        return self.workload.B
+
+    @property
+    def K(self):
+        return self.workload.K
+
+    @property
+    def V(self):
+        return self.workload.V
+
+    def k_of(self, b: int) -> int:
+        return self.workload.K if self.num_draft is None else int(self.num_draft[b])
+
+
+def _stored(x32: np.ndarray, dtype: str) -> np.ndarray:
+    return to_bf16_bits(x32) if dtype == "bf16" else x32
+
+
+def _as_f64(stored: np.ndarray, dtype: str) -> np.ndarray:
+    return (bf16_bits_to_f32(stored) if dtype == "bf16" else stored).astype(np.float64)
+
+
+def _gen_request(w: Workload, b: int, out: Inputs) -> None:
+    rng = np.random.default_rng(np.random.SeedSequence([w.seed, b]))
+    K, V = w.K, w.V
+    t32 = rng.standard_normal((K + 1, V), dtype=np.float32)
+    t32 *= np.float32(w.target_sigma)
+    if w.spike != 0.0:
+        idx = rng.integers(0, V, size=K + 1)
+        t32[np.arange(K + 1), idx] += np.float32(w.spike)
+    noise = rng.standard_normal((K, V), dtype=np.float32)
+    noise *= np.asarray(w.draft_sigma, dtype=np.float32)[:, None]
+    t_st = _stored(t32, w.dtype)
+    if w.identical_even and b % 2 == 0:
+        d_st = t_st[:K].copy()
+    else:
+        d_st = _stored(t32[:K] + noise, w.dtype)
+    d64 = _as_f64(d_st, w.dtype)
+    if w.mode == "sample":
+        e = rng.standard_exponential((K, V))  # float64: never exactly 0
+        keys = d64 / w.temperature - np.log(e)
+        x = np.argmax(keys, axis=1).astype(np.int32)
+    else:
+        x = np.argmax(d64, axis=1).astype(np.int32)
+    u = rng.random(K, dtype=np.float32)
+    r = rng.random(1, dtype=np.float32)[0]
+    k = int(rng.integers(1, K + 1)) if w.ragged else K
+    if k < K:
+        nan = BF16_NAN if w.dtype == "bf16" else np.float32(np.nan)
+        t_st[k + 1:] = nan
+        d_st[k:] = nan
+        x[k:] = -1
+        u[k:] = np.nan
+    out.target[b] = t_st
+    if out.draft is not None:
+        out.draft[b] = d_st
+    out.tokens[b] = x
+    out.uniforms[b] = u
+    out.residual[b] = r
+    if out.num_draft is not None:
+        out.num_draft[b] = k
+
+
+def generate(w: Workload, threads: Optional[int] = None) -> Inputs:
+    """Generate all B requests of workload `w` (requests are independent; threads share work)."""
+    st = np.uint16 if w.dtype == "bf16" else np.float32
+    out = Inputs(
+        workload=w,
+        target=np.empty((w.B, w.K + 1, w.V), dtype=st),
+        draft=np.empty((w.B, w.K, w.V), dtype=st) if w.mode == "sample" else None,
+        tokens=np.empty((w.B, w.K), dtype=np.int32),
+        uniforms=np.empty((w.B, w.K), dtype=np.float32),
+        residual=np.empty((w.B,), dtype=np.float32),
+        num_draft=np.empty((w.B,), dtype=np.int32) if w.ragged else None,
+    )
+    if threads is None:
+        threads = min(16, len(os.sched_getaffinity(0)))
+    if threads <= 1 or w.B == 1:
+        for b in range(w.B):
+            _gen_request(w, b, out)
+    else:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(lambda b: _gen_request(w, b, out), range(w.B)))
+    return out
