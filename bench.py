@@ -1,0 +1,215 @@
+"""Throughput of batched draft verification on one MI355X.
+
+python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--workload batched] [--out FILE]
+
+A step is one sv_verify_batch (or sv_verify_greedy) call over one batch of synthetic logits that
+is already resident in HBM. Several copies of the inputs at distinct addresses are rotated so that
+no step finds its rows in the 256 MB Infinity Cache from the previous step. Prints one JSON line:
+verified draft positions per second (the sum over requests of the drafts verified), with the
+achieved HBM bandwidth of the verify call against the MI355X peak, and the fp64 CPU oracle
+timed on a bounded sample of the same workload on this host.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("verified draft positions/sec and achieved HBM GB/s (% of peak) at V=151936, K=8")
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E peak
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="batched",
+                    help="tiny | interactive | batched | heavy | greedy | sweep_<mode>_<K>_<B>_<dtype>")
+    ap.add_argument("--min-rotation-bytes", type=float, default=1.2e9,
+                    help="rotate input copies until at least this many bytes are cycled")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU budget of the oracle baseline (0 = skip)")
+    ap.add_argument("--out", default=None, help="also append the JSON line to this file")
+    return ap.parse_args()
+
+
+def pick_workload(name):
+    import workloads as W
+
+    named = {"tiny": W.TINY, "interactive": W.INTERACTIVE, "batched": W.BATCHED,
+             "heavy": W.HEAVY, "greedy": W.GREEDY}
+    if name in named:
+        return named[name]
+    if name.startswith("sweep_"):
+        _, mode, k, b, dt = name.split("_")
+        return W.sweep_workload(int(k), int(b), dt, mode)
+    raise SystemExit(f"unknown workload {name}")
+
+
+def algorithmic_bytes(inp):
+    """Compulsory bytes of one call: every logit row the outputs depend on, read once, plus the
+    small per-request inputs and outputs."""
+    w = inp.workload
+    s = 2 if w.dtype == "bf16" else 4
+    ks = np.array([inp.k_of(b) for b in range(w.B)], dtype=np.int64)
+    rows = (2 * ks + 1) if w.mode == "sample" else (ks + 1)
+    logits = int(rows.sum()) * w.V * s
+    small = w.B * w.K * 4 + w.B * 4 * (1 if inp.num_draft is not None else 0)  # tokens, k_b
+    small += w.B * (w.K + 1) * 4 + w.B * 4  # committed, accepted_len
+    if w.mode == "sample":
+        small += w.B * w.K * 4 + w.B * 4 + w.B * w.K * 4  # uniforms, residual, target_prob
+    return logits + small, int(ks.sum())
+
+
+def cpu_baseline(inp, budget_s):
+    """The fp64 oracle, as it stands, on the first requests of the workload until the budget is
+    spent (at least one request). Single thread (numpy elementwise work)."""
+    import oracle
+
+    w = inp.workload
+    t0 = time.perf_counter()
+    done, positions = 0, 0
+    while done < w.B:
+        b = done
+        k = inp.k_of(b)
+        if w.mode == "sample":
+            oracle.verify_request(inp.target[b], inp.draft[b], w.dtype, inp.tokens[b],
+                                  inp.uniforms[b], float(inp.residual[b]), w.temperature, k,
+                                  w.K)
+        else:
+            oracle.verify_greedy_request(inp.target[b], w.dtype, inp.tokens[b], k, w.K)
+        done += 1
+        positions += k
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": positions / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {done} of {w.B} requests of {w.name} ({positions} positions, "
+                      f"{dt:.1f} s, fp64 numpy, one thread)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (requests are "
+                                   "independent: a multi-GPU run would shard the batch)"}))
+        sys.exit(2)
+
+    import torch
+
+    import lossless_draft_verification_sv_amd as sv
+    from workloads import generate
+
+    w = pick_workload(args.workload)
+    inp = generate(w)
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    t0 = up(inp.target)
+    d0 = up(inp.draft)
+    per_copy = t0.numel() * t0.element_size() + (0 if d0 is None else d0.numel() * d0.element_size())
+    copies = max(1, int(np.ceil(args.min_rotation_bytes / per_copy)))
+    targets = [t0] + [t0.clone() for _ in range(copies - 1)]
+    drafts = [d0] + ([d0.clone() for _ in range(copies - 1)] if d0 is not None else
+                     [None] * (copies - 1))
+    tokens, uniforms, residual = up(inp.tokens), up(inp.uniforms), up(inp.residual)
+    num_draft = up(inp.num_draft)
+    B, K, V = w.B, w.K, w.V
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    com = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+    tp = torch.empty(B, K, dtype=torch.float32, device=dev)
+    lib = sv.load_library()
+    nbytes = int(lib.sv_workspace_bytes(B, K, V))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    code = sv.SV_DTYPE_BF16 if w.dtype == "bf16" else sv.SV_DTYPE_F32
+    P = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+
+    def step(i):
+        c = i % copies
+        if w.mode == "sample":
+            st = lib.sv_verify_batch(P(targets[c]), P(drafts[c]), code, B, K, V,
+                                     float(w.temperature), P(tokens), P(num_draft), P(uniforms),
+                                     P(residual), P(acc), P(com), P(tp), None, P(ws), nbytes,
+                                     sptr)
+        else:
+            st = lib.sv_verify_greedy(P(targets[c]), code, B, K, V, P(tokens), P(num_draft),
+                                      P(acc), P(com), P(ws), nbytes, sptr)
+        if st != 0:
+            raise RuntimeError(f"sv call failed: {st} {sv.sv_last_error()}")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # per-call GPU time with events on the launch stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(args.warmup + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    ms_per_step = (t_end - t_start) * 1e3 / args.steps
+    call_us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    med_us = float(np.median(call_us))
+
+    alg_bytes, positions = algorithmic_bytes(inp)
+    acc_np = acc.cpu().numpy()
+    gbps = alg_bytes / (med_us * 1e-6) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": positions / (ms_per_step * 1e-3),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded numpy logits shaped like the pages' workloads; no dataset)",
+        "config": {"workload": w.name, "B": B, "K": K, "V": V, "logits": w.dtype,
+                   "temperature": w.temperature, "mode": w.mode,
+                   "ragged": inp.num_draft is not None, "input_copies_rotated": copies},
+        "achieved_gbps": gbps,
+        "hbm_peak_frac": gbps / HBM_PEAK_GBPS,
+        "call_us": {"median": med_us, "p10": float(np.percentile(call_us, 10)),
+                    "p90": float(np.percentile(call_us, 90))},
+        "positions_per_call": positions,
+        "algorithmic_bytes_per_call": alg_bytes,
+        "mean_acceptance_length": float(np.mean(acc_np + 1)),
+        "roofline": {"bound": "hbm", "kernel": "one verify call (all its launches)",
+                     "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None},
+    }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    line = json.dumps(result)
+    print(line, flush=True)
+    if args.out:
+        with open(args.out, "a") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

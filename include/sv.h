@@ -1,0 +1,115 @@
+/* sv.h — batched lossless draft verification for speculative decoding on MI355X (gfx950).
+ *
+ * The operation ("From draft-then-verify to DSpark", section "How speculative decoding works"):
+ * for every request b of a batch, the target model has scored k_b + 1 positions and the drafter
+ * has proposed k_b tokens x_0..x_{k_b-1}, each drawn from the draft distribution q_i. With p_i
+ * and q_i the softmaxes of the target and draft logits over the full vocabulary (both divided by
+ * one temperature), draft x_i is kept iff u_i < min(1, p_i(x_i) / q_i(x_i)). The longest run of
+ * kept drafts x_0..x_{n-1} is committed; at the first rejected slot n a token y is drawn from
+ * max(0, p_n - q_n) renormalised; if all k_b drafts are kept, y is drawn from p_{k_b} (the "+1"
+ * of the acceptance length in "Accelerating Large-Model Inference: Engineering Practice from
+ * Hidden-State Extraction to DSpark Speculative Decoding", section 1). Greedy mode ("Bringing
+ * DSpark to vLLM Metal") keeps drafts while x_i equals the target row's argmax and commits the
+ * target argmax at the first mismatch (or at row k_b).
+ *
+ * Conventions shared by every entry point:
+ *  - All array pointers are DEVICE pointers (hipMalloc / torch CUDA tensors on a ROCm build),
+ *    owned by the caller. Arrays are row-major and contiguous. Nothing is allocated and nothing
+ *    synchronises the host: work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *    stream) and outputs are valid once the stream has reached that point.
+ *  - Return value: SV_OK, or a negative sv_status. Arguments are validated on the host before
+ *    anything is enqueued; on a validation error nothing is launched and no output is written.
+ *    SV_ERR_HIP reports a launch failure. sv_last_error() gives a message for the last failing
+ *    call on the calling thread.
+ *  - Limits: 1 <= B <= 1048576, 1 <= K <= 64, 1 <= V <= 67108864; a batch whose launch would
+ *    need 2^24 or more work-groups (B * (2K+1) rows and more) returns SV_ERR_UNSUPPORTED.
+ *  - Device-side preconditions are not checked (checking would cost a pass over the data):
+ *    draft tokens of verified slots lie in [0, V) and every row that is read has at least one
+ *    finite logit; NaN and +inf logits give undefined results. For memory safety a token outside
+ *    [0, V) is treated as p(x) = q(x) = 0 (rejected; its target_prob is 0) and num_draft values
+ *    are clamped to [0, K].
+ *  - Rows a request does not verify (target rows past k_b, draft rows from k_b on) are never
+ *    read, and may hold anything.
+ *  - The workspace (at least sv_workspace_bytes(B, K, V) bytes, any contents, 8-byte aligned)
+ *    holds per-chunk partial results and per-request counters. One workspace must not be used
+ *    by two calls that can run at the same time.
+ */
+#ifndef SV_H_
+#define SV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SV_OK = 0,
+  SV_ERR_INVALID_ARG = -1, /* a size, pointer, dtype or temperature is out of range */
+  SV_ERR_UNSUPPORTED = -2, /* a valid request this build does not handle */
+  SV_ERR_WORKSPACE = -3,   /* workspace missing, misaligned or smaller than required */
+  SV_ERR_HIP = -4          /* the HIP runtime refused a launch */
+} sv_status;
+
+typedef enum {
+  SV_DTYPE_F32 = 0, /* IEEE float32 logits */
+  SV_DTYPE_BF16 = 1 /* bfloat16 logits (the upper 16 bits of a float32) */
+} sv_dtype;
+
+/* Bytes of device workspace that sv_verify_batch and sv_verify_greedy need for a batch of
+ * shape (B, K, V); 0 if the shape is outside the limits. Host-only, no GPU call. */
+size_t sv_workspace_bytes(int B, int K, int V);
+
+/* Static text for a status code. */
+const char* sv_status_string(int status);
+
+/* Message describing the last failing call made on this thread ("" if none). */
+const char* sv_last_error(void);
+
+/* Sampling-mode verification ("From draft-then-verify to DSpark", "How speculative decoding
+ * works": the min(1, p/q) acceptance test, the longest accepted prefix, the residual draw from
+ * max(0, p - q), and the extra draw from the target when every draft is kept).
+ *
+ *  target_logits     [B, K+1, V] dtype   target scores of the K+1 positions of each request
+ *  draft_logits      [B, K,   V] dtype   the draft logits each draft token was drawn from
+ *  dtype             sv_dtype of both logit arrays
+ *  temperature       > 0, finite; both p and q are softmax(logits / temperature)
+ *  draft_tokens      [B, K] int32        proposals x_i
+ *  num_draft         [B] int32 or NULL   k_b, drafts to verify per request (NULL: all K)
+ *  uniforms          [B, K] float32      u_i in [0, 1): slot i is kept iff u_i < min(1, p/q)
+ *  residual_uniform  [B] float32         r in [0, 1): drives the residual draw or the extra draw
+ *                                        (inverse CDF in ascending vocabulary order: the token
+ *                                        is the smallest v with sum_{j<=v} w_j > r * sum_j w_j)
+ *  accepted_len      [B] int32 out       n = number of kept drafts, 0..k_b
+ *  committed         [B, K+1] int32 out  x_0..x_{n-1}, y, then -1 padding
+ *  target_prob       [B, K] float32 out  p_i(x_i) for i < k_b, 0 for i >= k_b
+ *  draft_prob        [B, K] float32 out or NULL: q_i(x_i) for i < k_b, 0 for i >= k_b
+ *  workspace, workspace_bytes            scratch, see above
+ *  stream                                hipStream_t
+ */
+int sv_verify_batch(const void* target_logits, const void* draft_logits, int dtype, int B, int K,
+                    int V, float temperature, const int32_t* draft_tokens,
+                    const int32_t* num_draft, const float* uniforms,
+                    const float* residual_uniform, int32_t* accepted_len, int32_t* committed,
+                    float* target_prob, float* draft_prob, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Greedy-mode verification ("Bringing DSpark to vLLM Metal": greedy serving whose output ids
+ * equal target-only greedy decoding). g_i = argmax_v target_logits[b, i, v] compared on the
+ * stored values, lowest index on ties. n = first i < k_b with x_i != g_i, else k_b.
+ *
+ *  target_logits  [B, K+1, V] dtype;  draft_tokens [B, K] int32;  num_draft [B] int32 or NULL
+ *  accepted_len   [B] int32 out: n;   committed [B, K+1] int32 out: x_0..x_{n-1}, g_n, -1...
+ *  Draft logits are not needed: the proposals already are the drafter's greedy choices.
+ */
+int sv_verify_greedy(const void* target_logits, int dtype, int B, int K, int V,
+                     const int32_t* draft_tokens, const int32_t* num_draft,
+                     int32_t* accepted_len, int32_t* committed, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SV_H_ */

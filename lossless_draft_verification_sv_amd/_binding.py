@@ -1,0 +1,188 @@
+"""ctypes binding of libsv.so: argument marshalling only.
+
+Every step of verification runs in the HIP kernels behind the C ABI (include/sv.h). This module
+turns torch tensors into device pointers, allocates outputs and the workspace with torch on the
+tensors' device, and passes torch's current HIP stream. If the library is missing it raises;
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import NamedTuple, Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_PATH = os.path.join(_PKG, "libsv.so")
+
+SV_OK = 0
+SV_ERR_INVALID_ARG = -1
+SV_ERR_UNSUPPORTED = -2
+SV_ERR_WORKSPACE = -3
+SV_ERR_HIP = -4
+SV_DTYPE_F32 = 0
+SV_DTYPE_BF16 = 1
+
+_lock = threading.Lock()
+_lib = None
+
+
+class SVError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"sv status {status}: {message}")
+        self.status = status
+
+
+def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
+    """Load libsv.so once and declare the C signatures. Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it with `python -m "
+                "lossless_draft_verification_sv_amd.build` (hipcc, gfx950)")
+        lib = ctypes.CDLL(path)
+        vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        lib.sv_workspace_bytes.argtypes = [i32, i32, i32]
+        lib.sv_workspace_bytes.restype = sz
+        lib.sv_status_string.argtypes = [i32]
+        lib.sv_status_string.restype = ctypes.c_char_p
+        lib.sv_last_error.argtypes = []
+        lib.sv_last_error.restype = ctypes.c_char_p
+        lib.sv_verify_batch.argtypes = [vp, vp, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp,
+                                        vp, vp, vp, sz, vp]
+        lib.sv_verify_batch.restype = i32
+        lib.sv_verify_greedy.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+        lib.sv_verify_greedy.restype = i32
+        _lib = lib
+        return lib
+
+
+def sv_workspace_bytes(B: int, K: int, V: int) -> int:
+    return int(load_library().sv_workspace_bytes(B, K, V))
+
+
+def sv_status_string(status: int) -> str:
+    return load_library().sv_status_string(status).decode()
+
+
+def sv_last_error() -> str:
+    return load_library().sv_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != SV_OK:
+        raise SVError(status, f"{sv_status_string(status)}: {sv_last_error()}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SV_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return SV_DTYPE_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape, device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_ws_cache = {}
+
+
+def _workspace(device: torch.device, stream: int, nbytes: int) -> torch.Tensor:
+    """One cached workspace per (device, stream): calls on one stream never overlap."""
+    key = (device, stream)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+class VerifyOutput(NamedTuple):
+    accepted_len: torch.Tensor  # [B] int32
+    committed: torch.Tensor  # [B, K+1] int32
+    target_prob: Optional[torch.Tensor]  # [B, K] float32 (sampling mode)
+    draft_prob: Optional[torch.Tensor]  # [B, K] float32 (sampling mode, on request)
+
+
+def sv_verify_batch(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
+                    uniforms: torch.Tensor, residual_uniform: torch.Tensor,
+                    temperature: float = 1.0, num_draft: Optional[torch.Tensor] = None,
+                    return_draft_prob: bool = False) -> VerifyOutput:
+    """Sampling-mode verification on the tensors' GPU (see sv_verify_batch in include/sv.h).
+
+    target [B, K+1, V] and draft [B, K, V]: float32 or bfloat16 logits; draft_tokens [B, K]
+    int32; uniforms [B, K] float32; residual_uniform [B] float32; num_draft [B] int32 or None.
+    """
+    lib = load_library()
+    if target.dim() != 3:
+        raise ValueError("target must be [B, K+1, V]")
+    B, K1, V = target.shape
+    K = K1 - 1
+    dev = target.device
+    if dev.type != "cuda":
+        raise ValueError("target must be a GPU tensor")
+    _need(draft, "draft", target.dtype, (B, K, V), dev)
+    _need(target, "target", target.dtype, (B, K + 1, V), dev)
+    _need(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
+    _need(uniforms, "uniforms", torch.float32, (B, K), dev)
+    _need(residual_uniform, "residual_uniform", torch.float32, (B,), dev)
+    if num_draft is not None:
+        _need(num_draft, "num_draft", torch.int32, (B,), dev)
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    com = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+    tp = torch.empty(B, K, dtype=torch.float32, device=dev)
+    dp = torch.empty(B, K, dtype=torch.float32, device=dev) if return_draft_prob else None
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    nbytes = int(lib.sv_workspace_bytes(B, K, V))
+    ws = _workspace(dev, stream, nbytes)
+    _check(lib.sv_verify_batch(
+        _ptr(target), _ptr(draft), _dtype_code(target), B, K, V, float(temperature),
+        _ptr(draft_tokens), _ptr(num_draft), _ptr(uniforms), _ptr(residual_uniform), _ptr(acc),
+        _ptr(com), _ptr(tp), _ptr(dp), _ptr(ws), ws.numel(), stream))
+    return VerifyOutput(acc, com, tp, dp)
+
+
+def sv_verify_greedy(target: torch.Tensor, draft_tokens: torch.Tensor,
+                     num_draft: Optional[torch.Tensor] = None) -> VerifyOutput:
+    """Greedy-mode verification on the tensors' GPU (see sv_verify_greedy in include/sv.h)."""
+    lib = load_library()
+    if target.dim() != 3:
+        raise ValueError("target must be [B, K+1, V]")
+    B, K1, V = target.shape
+    K = K1 - 1
+    dev = target.device
+    if dev.type != "cuda":
+        raise ValueError("target must be a GPU tensor")
+    _need(target, "target", target.dtype, (B, K + 1, V), dev)
+    _need(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
+    if num_draft is not None:
+        _need(num_draft, "num_draft", torch.int32, (B,), dev)
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    com = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    nbytes = int(lib.sv_workspace_bytes(B, K, V))
+    ws = _workspace(dev, stream, nbytes)
+    _check(lib.sv_verify_greedy(
+        _ptr(target), _dtype_code(target), B, K, V, _ptr(draft_tokens), _ptr(num_draft),
+        _ptr(acc), _ptr(com), _ptr(ws), ws.numel(), stream))
+    return VerifyOutput(acc, com, None, None)

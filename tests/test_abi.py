@@ -1,0 +1,138 @@
+"""The C-ABI library on the host (CPU only; no call here reaches the GPU).
+
+Checks that libsv.so loads, exports every function include/sv.h declares, answers the host-only
+queries, and rejects invalid arguments with the documented status before launching anything.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import lossless_draft_verification_sv_amd as sv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sv.LIBRARY_PATH):
+        pytest.skip("libsv.so not built")
+    return sv.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"sv_verify_batch", "sv_verify_greedy", "sv_workspace_bytes"} <= set(names)
+    raw = ctypes.CDLL(sv.LIBRARY_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_status_strings(lib):
+    for code in (sv.SV_OK, sv.SV_ERR_INVALID_ARG, sv.SV_ERR_UNSUPPORTED, sv.SV_ERR_WORKSPACE,
+                 sv.SV_ERR_HIP):
+        assert sv.sv_status_string(code)
+    assert sv.sv_status_string(12345) == "unknown status"
+
+
+def test_workspace_bytes(lib):
+    assert sv.sv_workspace_bytes(0, 8, 100) == 0
+    assert sv.sv_workspace_bytes(1, 0, 100) == 0
+    assert sv.sv_workspace_bytes(1, 65, 100) == 0
+    assert sv.sv_workspace_bytes(1, 8, 0) == 0
+    a = sv.sv_workspace_bytes(64, 8, 151936)
+    b = sv.sv_workspace_bytes(256, 16, 151936)
+    assert 0 < a < 64 << 20 and 0 < b < 64 << 20
+    assert a % 256 == 0
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+WS = 0x2000
+
+
+def call_batch(lib, **kw):
+    args = dict(target=FAKE, draft=FAKE, dtype=sv.SV_DTYPE_BF16, B=2, K=4, V=1000,
+                temperature=1.0, tokens=FAKE, num_draft=None, uniforms=FAKE, residual=FAKE,
+                acc=FAKE, com=FAKE, tp=FAKE, dp=None, ws=WS, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return lib.sv_verify_batch(*args.values())
+
+
+def call_greedy(lib, **kw):
+    args = dict(target=FAKE, dtype=sv.SV_DTYPE_F32, B=2, K=4, V=1000, tokens=FAKE,
+                num_draft=None, acc=FAKE, com=FAKE, ws=WS, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return lib.sv_verify_greedy(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), sv.SV_ERR_INVALID_ARG),
+    (dict(B=(1 << 20) + 1), sv.SV_ERR_INVALID_ARG),
+    (dict(K=0), sv.SV_ERR_INVALID_ARG),
+    (dict(K=65), sv.SV_ERR_INVALID_ARG),
+    (dict(V=0), sv.SV_ERR_INVALID_ARG),
+    (dict(dtype=7), sv.SV_ERR_INVALID_ARG),
+    (dict(target=None), sv.SV_ERR_INVALID_ARG),
+    (dict(draft=None), sv.SV_ERR_INVALID_ARG),
+    (dict(tokens=None), sv.SV_ERR_INVALID_ARG),
+    (dict(uniforms=None), sv.SV_ERR_INVALID_ARG),
+    (dict(residual=None), sv.SV_ERR_INVALID_ARG),
+    (dict(acc=None), sv.SV_ERR_INVALID_ARG),
+    (dict(com=None), sv.SV_ERR_INVALID_ARG),
+    (dict(tp=None), sv.SV_ERR_INVALID_ARG),
+    (dict(temperature=0.0), sv.SV_ERR_INVALID_ARG),
+    (dict(temperature=-1.0), sv.SV_ERR_INVALID_ARG),
+    (dict(temperature=float("nan")), sv.SV_ERR_INVALID_ARG),
+    (dict(temperature=float("inf")), sv.SV_ERR_INVALID_ARG),
+    (dict(temperature=1e-9), sv.SV_ERR_INVALID_ARG),
+    (dict(ws=None), sv.SV_ERR_WORKSPACE),
+    (dict(ws=WS + 4), sv.SV_ERR_WORKSPACE),
+    (dict(ws_bytes=16), sv.SV_ERR_WORKSPACE),
+])
+def test_batch_rejects_invalid_arguments(lib, kw, status):
+    assert call_batch(lib, **kw) == status
+    assert sv.sv_last_error() != ""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), sv.SV_ERR_INVALID_ARG),
+    (dict(K=0), sv.SV_ERR_INVALID_ARG),
+    (dict(K=65), sv.SV_ERR_INVALID_ARG),
+    (dict(V=(1 << 26) + 1), sv.SV_ERR_INVALID_ARG),
+    (dict(dtype=-1), sv.SV_ERR_INVALID_ARG),
+    (dict(target=None), sv.SV_ERR_INVALID_ARG),
+    (dict(tokens=None), sv.SV_ERR_INVALID_ARG),
+    (dict(acc=None), sv.SV_ERR_INVALID_ARG),
+    (dict(com=None), sv.SV_ERR_INVALID_ARG),
+    (dict(ws=None), sv.SV_ERR_WORKSPACE),
+    (dict(ws_bytes=0), sv.SV_ERR_WORKSPACE),
+])
+def test_greedy_rejects_invalid_arguments(lib, kw, status):
+    assert call_greedy(lib, **kw) == status
+    assert sv.sv_last_error() != ""
+
+
+def test_workspace_size_is_exactly_enough(lib):
+    need = sv.sv_workspace_bytes(2, 4, 1000)
+    assert call_batch(lib, ws_bytes=need - 1) == sv.SV_ERR_WORKSPACE
+    assert call_greedy(lib, ws_bytes=need - 1) == sv.SV_ERR_WORKSPACE
+
+
+def test_python_binding_rejects_bad_tensors():
+    import torch
+
+    t = torch.zeros(2, 5, 10)
+    with pytest.raises(ValueError):
+        sv.sv_verify_batch(t, torch.zeros(2, 4, 10), torch.zeros(2, 4, dtype=torch.int32),
+                           torch.zeros(2, 4), torch.zeros(2))  # CPU tensors
+    with pytest.raises((TypeError, ValueError)):
+        sv.sv_verify_greedy(torch.zeros(2, 5, 10, dtype=torch.float64),
+                            torch.zeros(2, 4, dtype=torch.int32))

@@ -1,0 +1,158 @@
+"""Sampling-mode parity of the HIP path with the fp64 oracle (GPU).
+
+Small shapes span several work-groups, vector and scalar row paths and ragged chunk tails; the
+full-size cases are the workloads the benchmark times, in the same launch configuration.
+"""
+import glob
+import json
+import os
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+from tests.gpu_util import check_sample_parity, run_sample, say  # noqa: E402
+from workloads import (BATCHED, HEAVY, INTERACTIVE, TINY, generate, to_bf16_bits)  # noqa: E402
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _check(inp, requests=None, name=None):
+    w = inp.workload
+    return check_sample_parity(name or w.name, inp.target, inp.draft, w.dtype, inp.tokens,
+                               inp.uniforms, inp.residual, w.temperature, inp.num_draft,
+                               requests=requests)
+
+
+def test_tiny_workload_exact():
+    s = _check(generate(TINY))
+    assert s["ambiguous"] == 0
+
+
+SMALL = [
+    # (B, K, V, dtype, tau, ragged, identical_even)
+    (3, 4, 1000, "f32", 1.0, False, False),  # 16-byte rows: vector loads
+    (5, 3, 4099, "f32", 0.8, False, False),  # odd V: scalar path
+    (4, 6, 4099, "bf16", 1.3, False, True),  # scalar bf16, half identical
+    (6, 8, 16400, "bf16", 0.7, False, True),  # vector bf16, several chunks per row
+    (7, 5, 12288, "f32", 2.0, True, False),  # ragged k_b, NaN rows past k_b
+    (9, 16, 6000, "bf16", 1.0, True, False),  # ragged, K=16
+    (2, 1, 70000, "bf16", 0.5, False, False),  # K=1
+    (3, 64, 520, "f32", 1.0, False, False),  # K=64: every slot in one wave
+]
+
+
+@pytest.mark.parametrize("B,K,V,dtype,tau,ragged,ident", SMALL)
+def test_small_shapes(B, K, V, dtype, tau, ragged, ident):
+    w = HEAVY.replace(name=f"small_B{B}_K{K}_V{V}_{dtype}_t{tau}", B=B, K=K, V=V, dtype=dtype,
+                      temperature=tau, ragged=ragged, identical_even=ident,
+                      seed=3000 + B * 7 + K * 3 + V)
+    _check(generate(w))
+
+
+def test_identical_rows_accept_every_draft():
+    inp = generate(BATCHED.replace(B=8, V=20000, seed=31))
+    even = np.arange(0, 8, 2)
+    s = _check(inp)
+    acc, _, _, _ = run_sample(inp.target, inp.draft, inp.tokens, inp.uniforms, inp.residual,
+                              inp.workload.temperature)
+    assert np.all(acc[even] == inp.workload.K)
+
+
+def test_zero_drafts_and_out_of_range_tokens():
+    w = TINY.replace(B=6, K=5, V=3000, seed=41)
+    inp = generate(w)
+    nd = np.array([0, 5, 2, 0, 5, 1], dtype=np.int32)
+    inp.num_draft = nd
+    inp.tokens[1, 0] = 3000 + 7  # past the vocabulary: rejected, p = 0
+    inp.tokens[4, 2] = -3
+    s = _check(inp, name="k0_and_out_of_range")
+    acc, com, tp, _ = run_sample(inp.target, inp.draft, inp.tokens, inp.uniforms, inp.residual,
+                                 w.temperature, nd)
+    assert acc[0] == 0 and acc[3] == 0 and acc[1] == 0 and tp[1, 0] == 0.0
+    assert acc[4] <= 2
+
+
+def test_misaligned_rows_take_the_scalar_path():
+    import torch
+
+    import lossless_draft_verification_sv_amd as sv
+    import oracle
+
+    inp = generate(TINY.replace(B=3, K=4, V=4096, seed=51))
+    w = inp.workload
+    dev = torch.device("cuda:0")
+
+    def shifted(a):  # same values, device pointer 4 bytes past a 16-byte boundary
+        flat = torch.empty(a.size + 1, dtype=torch.float32, device=dev)
+        view = flat[1:].view(a.shape)
+        view.copy_(torch.from_numpy(a))
+        return view
+
+    t, d = shifted(inp.target), shifted(inp.draft)
+    assert t.data_ptr() % 16 != 0
+    out = sv.sv_verify_batch(t, d, torch.from_numpy(inp.tokens).to(dev),
+                             torch.from_numpy(inp.uniforms).to(dev),
+                             torch.from_numpy(inp.residual).to(dev), w.temperature)
+    torch.cuda.synchronize()
+    ref = oracle.verify_batch(inp.target, inp.draft, "f32", inp.tokens, inp.uniforms,
+                              inp.residual, w.temperature)
+    ok = ~ref.ambiguous
+    assert np.array_equal(out.committed.cpu().numpy()[ok], ref.committed[ok])
+    assert np.max(np.abs(out.target_prob.cpu().numpy() - ref.target_prob)) <= 1e-5
+
+
+@pytest.mark.parametrize("tau", [0.05, 20.0])
+def test_extreme_temperatures(tau):
+    w = TINY.replace(name=f"temperature_{tau}", B=6, K=4, V=8000, dtype="bf16",
+                     temperature=tau, seed=61)
+    _check(generate(w))
+
+
+def test_golden_worked_examples_on_gpu():
+    for f in sorted(glob.glob(os.path.join(GOLDEN, "*.json"))):
+        g = json.load(open(f))
+        if g["mode"] != "sample":
+            continue
+        T = np.log(np.asarray(g["target_probs"], dtype=np.float64)).astype(np.float32)[None]
+        D = np.log(np.asarray(g["draft_probs"], dtype=np.float64)).astype(np.float32)[None]
+        x = np.asarray([g["tokens"]], dtype=np.int32)
+        u = np.asarray([g["uniforms"]], dtype=np.float32)
+        r = np.asarray([g["residual"]], dtype=np.float32)
+        acc, com, tp, dp = run_sample(T, D, x, u, r, g["tau"])
+        e = g["expected"]
+        say(f"[gpu] golden {os.path.basename(f)}: {acc.tolist()} {com.tolist()}")
+        assert acc[0] == e["accepted_len"] and com[0].tolist() == e["committed"], f
+        assert np.allclose(tp[0], e["target_prob"], atol=1e-6), f
+        assert np.allclose(dp[0], e["draft_prob"], atol=1e-6), f
+
+
+def test_repeat_calls_are_bitwise_deterministic():
+    inp = generate(BATCHED.replace(B=6, V=30000, seed=71))
+    w = inp.workload
+    a = run_sample(inp.target, inp.draft, inp.tokens, inp.uniforms, inp.residual, w.temperature)
+    for _ in range(5):
+        b = run_sample(inp.target, inp.draft, inp.tokens, inp.uniforms, inp.residual,
+                       w.temperature)
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
+
+
+# ----- full sizes (V = 151936), the configurations the benchmark times ---------------------
+
+
+def test_full_interactive_B1_K8_f32():
+    _check(generate(INTERACTIVE))
+
+
+def test_full_batched_B64_K8_bf16():
+    s = _check(generate(BATCHED))
+    assert s["requests"] == 64
+
+
+def test_full_heavy_B256_K16_bf16_sampled_requests():
+    inp = generate(HEAVY)
+    rng = np.random.default_rng(0)
+    req = sorted(rng.choice(HEAVY.B, size=40, replace=False).tolist())
+    _check(inp, requests=req)
