@@ -134,7 +134,7 @@ def main():
     tp = torch.empty(B, K, dtype=torch.float32, device=dev)
     lib = sv.load_library()
     nbytes = int(lib.sv_workspace_bytes(B, K, V))
-    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)  # zero-filled once
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
     code = sv.SV_DTYPE_BF16 if w.dtype == "bf16" else sv.SV_DTYPE_F32

@@ -108,11 +108,12 @@ _ws_cache = {}
 
 
 def _workspace(device: torch.device, stream: int, nbytes: int) -> torch.Tensor:
-    """One cached workspace per (device, stream): calls on one stream never overlap."""
+    """One cached, zero-filled workspace per (device, stream): calls on one stream never
+    overlap, and every call leaves the workspace's counters at zero for the next."""
     key = (device, stream)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _ws_cache[key] = ws
     return ws
 

@@ -20,18 +20,24 @@ from tests.gpu_util import run_sample, say  # noqa: E402
 @pytest.mark.parametrize("V,K,tau,seed", [(5, 1, 1.0, 1), (8, 2, 0.8, 2), (6, 3, 1.3, 3)])
 def test_committed_tokens_follow_the_target(V, K, tau, seed):
     rng = np.random.default_rng(seed)
-    B = 200_000
+    B, calls = 50_000, 4  # 200000 rounds in four batches
     T1 = rng.normal(0, 1.5, size=(K + 1, V)).astype(np.float32)
     D1 = (T1[:K] + rng.normal(0, 1.0, size=(K, V))).astype(np.float32)
     p = [scipy.special.softmax(T1[i].astype(np.float64) / tau) for i in range(K + 1)]
     q = [scipy.special.softmax(D1[i].astype(np.float64) / tau) for i in range(K)]
     T = np.ascontiguousarray(np.broadcast_to(T1, (B, K + 1, V)))
     D = np.ascontiguousarray(np.broadcast_to(D1, (B, K, V)))
-    x = np.stack([rng.choice(V, size=B, p=q[i]) for i in range(K)], axis=1).astype(np.int32)
-    u = rng.random((B, K), dtype=np.float32)
-    r = rng.random(B, dtype=np.float32)
-    say(f"[gpu] law V={V} K={K} tau={tau} B={B}")
-    acc, com, _, _ = run_sample(T, D, x, u, r, tau)
+    say(f"[gpu] law V={V} K={K} tau={tau} rounds={B * calls}")
+    accs, coms = [], []
+    for _ in range(calls):
+        x = np.stack([rng.choice(V, size=B, p=q[i]) for i in range(K)], axis=1).astype(np.int32)
+        u = rng.random((B, K), dtype=np.float32)
+        r = rng.random(B, dtype=np.float32)
+        a_, c_, _, _ = run_sample(T, D, x, u, r, tau)
+        accs.append(a_)
+        coms.append(c_)
+    acc, com = np.concatenate(accs), np.concatenate(coms)
+    B = B * calls
 
     beta = [float(np.sum(np.minimum(p[j], q[j]))) for j in range(K)]
     pn = np.array([np.prod(beta[:i]) * ((1 - beta[i]) if i < K else 1.0) for i in range(K + 1)])

@@ -156,3 +156,51 @@ def test_full_heavy_B256_K16_bf16_sampled_requests():
     rng = np.random.default_rng(0)
     req = sorted(rng.choice(HEAVY.B, size=40, replace=False).tolist())
     _check(inp, requests=req)
+
+
+def test_one_workspace_reused_across_shapes_and_modes():
+    """Every call leaves the workspace's counters at zero: a single zero-filled workspace serves
+    calls of different shapes and both modes in sequence, each matching the oracle."""
+    import torch
+
+    import lossless_draft_verification_sv_amd as sv
+    import oracle
+    from tests.gpu_util import to_dev
+
+    lib = sv.load_library()
+    dev = torch.device("cuda:0")
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=dev)
+    s = torch.cuda.current_stream().cuda_stream
+    shapes = [(5, 8, 30000, "bf16"), (2, 3, 4099, "f32"), (9, 16, 20000, "bf16"),
+              (1, 4, 1000, "f32"), (5, 8, 30000, "bf16")]
+    for i, (B, K, V, dt) in enumerate(shapes * 2):
+        w = BATCHED.replace(name=f"reuse{i}", B=B, K=K, V=V, dtype=dt, temperature=1.0,
+                            seed=900 + i)
+        inp = generate(w)
+        T, D = to_dev(inp.target), to_dev(inp.draft)
+        x, u, r = to_dev(inp.tokens), to_dev(inp.uniforms), to_dev(inp.residual)
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+        com = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+        tp = torch.empty(B, K, dtype=torch.float32, device=dev)
+        code = sv.SV_DTYPE_BF16 if dt == "bf16" else sv.SV_DTYPE_F32
+        if i % 2 == 0:
+            st = lib.sv_verify_batch(T.data_ptr(), D.data_ptr(), code, B, K, V, 1.0,
+                                     x.data_ptr(), None, u.data_ptr(), r.data_ptr(),
+                                     acc.data_ptr(), com.data_ptr(), tp.data_ptr(), None,
+                                     ws.data_ptr(), ws.numel(), s)
+            assert st == 0, sv.sv_last_error()
+            torch.cuda.synchronize()
+            ref = oracle.verify_batch(inp.target, inp.draft, dt, inp.tokens, inp.uniforms,
+                                      inp.residual, 1.0)
+            ok = ~ref.ambiguous
+            assert np.array_equal(com.cpu().numpy()[ok], ref.committed[ok]), i
+        else:
+            st = lib.sv_verify_greedy(T.data_ptr(), code, B, K, V, x.data_ptr(), None,
+                                      acc.data_ptr(), com.data_ptr(), ws.data_ptr(), ws.numel(),
+                                      s)
+            assert st == 0, sv.sv_last_error()
+            torch.cuda.synchronize()
+            ref = oracle.verify_greedy(inp.target, dt, inp.tokens)
+            assert np.array_equal(com.cpu().numpy(), ref.committed), i
+    # the counter region at the front of the workspace is back to zero
+    assert int(ws[: 2 * 4 * 65536].sum().item()) == 0
