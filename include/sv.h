@@ -21,7 +21,7 @@
  *    anything is enqueued; on a validation error nothing is launched and no output is written.
  *    SV_ERR_HIP reports a launch failure. sv_last_error() gives a message for the last failing
  *    call on the calling thread.
- *  - Limits: 1 <= B <= 65536, 1 <= K <= 64, 1 <= V <= 67108864; a batch whose launch would
+ *  - Limits: 1 <= B <= 1048576, 1 <= K <= 64, 1 <= V <= 67108864; a batch whose launch would
  *    need 2^24 or more work-groups (B * (2K+1) rows and more) returns SV_ERR_UNSUPPORTED.
  *  - Device-side preconditions are not checked (checking would cost a pass over the data):
  *    draft tokens of verified slots lie in [0, V) and every row that is read has at least one
@@ -31,15 +31,15 @@
  *  - Rows a request does not verify (target rows past k_b, draft rows from k_b on) are never
  *    read, and may hold anything.
  *  - The workspace: at least sv_workspace_bytes(B, K, V) bytes, 256-byte aligned, owned by the
- *    caller. It holds per-request arrival counters (a fixed region at its start) and per-chunk
- *    partial results. It must be zero-filled once before its first use (hipMemset, or
- *    torch.zeros); every call returns the counters to zero, so later calls of any shape may
- *    reuse it without clearing. One workspace must not be used by two calls that can run at
- *    the same time (e.g. on two streams).
- *  - Within one call, work-groups hand partial results to each other through the workspace and
- *    per-request counters; a work-group that waits for its request's partials gives up after a
+ *    caller. Within one call, work-groups hand per-chunk partial results to each other through
+ *    it, each value stamped with a number drawn fresh for every call, so nothing needs clearing
+ *    between calls, of any shape. Zero-fill it once before first use (hipMemset or
+ *    torch.zeros): a word of a never-written workspace whose upper half happened to equal a
+ *    call's number would be taken for that call's data. One workspace must not be used by two
+ *    calls that can run at the same time (e.g. on two streams).
+ *  - A work-group waiting for partials from other work-groups of the same call gives up after a
  *    bounded time (about two seconds) and then stores -2 in that request's accepted_len. This
- *    does not happen in normal operation; it reports a workspace that was not zero-filled.
+ *    does not happen in normal operation.
  */
 #ifndef SV_H_
 #define SV_H_

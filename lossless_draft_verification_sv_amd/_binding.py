@@ -108,8 +108,8 @@ _ws_cache = {}
 
 
 def _workspace(device: torch.device, stream: int, nbytes: int) -> torch.Tensor:
-    """One cached, zero-filled workspace per (device, stream): calls on one stream never
-    overlap, and every call leaves the workspace's counters at zero for the next."""
+    """One cached workspace per (device, stream), zero-filled when allocated: calls on one
+    stream never overlap, and a workspace needs no clearing between calls."""
     key = (device, stream)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:

@@ -48,7 +48,7 @@ def test_workspace_bytes(lib):
     assert sv.sv_workspace_bytes(1, 0, 100) == 0
     assert sv.sv_workspace_bytes(1, 65, 100) == 0
     assert sv.sv_workspace_bytes(1, 8, 0) == 0
-    assert sv.sv_workspace_bytes(65537, 8, 100) == 0
+    assert sv.sv_workspace_bytes((1 << 20) + 1, 8, 100) == 0
     a = sv.sv_workspace_bytes(64, 8, 151936)
     b = sv.sv_workspace_bytes(256, 16, 151936)
     assert 0 < a < 64 << 20 and 0 < b < 64 << 20
@@ -76,7 +76,7 @@ def call_greedy(lib, **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(B=0), sv.SV_ERR_INVALID_ARG),
-    (dict(B=(1 << 16) + 1), sv.SV_ERR_INVALID_ARG),
+    (dict(B=(1 << 20) + 1), sv.SV_ERR_INVALID_ARG),
     (dict(K=0), sv.SV_ERR_INVALID_ARG),
     (dict(K=65), sv.SV_ERR_INVALID_ARG),
     (dict(V=0), sv.SV_ERR_INVALID_ARG),

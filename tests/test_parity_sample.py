@@ -159,8 +159,9 @@ def test_full_heavy_B256_K16_bf16_sampled_requests():
 
 
 def test_one_workspace_reused_across_shapes_and_modes():
-    """Every call leaves the workspace's counters at zero: a single zero-filled workspace serves
-    calls of different shapes and both modes in sequence, each matching the oracle."""
+    """A single zero-filled workspace serves calls of different shapes and both modes in
+    sequence, each matching the oracle: partials left by earlier calls are never taken for the
+    current call's."""
     import torch
 
     import lossless_draft_verification_sv_amd as sv
@@ -202,5 +203,3 @@ def test_one_workspace_reused_across_shapes_and_modes():
             torch.cuda.synchronize()
             ref = oracle.verify_greedy(inp.target, dt, inp.tokens)
             assert np.array_equal(com.cpu().numpy(), ref.committed), i
-    # the counter region at the front of the workspace is back to zero
-    assert int(ws[: 2 * 4 * 65536].sum().item()) == 0
