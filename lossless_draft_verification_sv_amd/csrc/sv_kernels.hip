@@ -144,17 +144,31 @@ __device__ __forceinline__ uint64_t fetch(const uint64_t* p) {
 }
 __device__ __forceinline__ bool tagged(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
 
-// Thread 0 of a waiting group watches one word until it carries the tag, spending from the
-// group's budget of polls (shared by every wait of the group, so the total wait is bounded).
-__device__ __forceinline__ void watch(const uint64_t* word, uint32_t tag, int* budget) {
-  if (threadIdx.x == 0) {
-    int left = *budget;
-    while (left > 0 && !tagged(fetch(word), tag)) --left;
-    *budget = left - 1;  // a full check costs one poll too
-  }
-  __syncthreads();
-}
 __device__ __forceinline__ uint32_t payload(uint64_t w) { return (uint32_t)w; }
+
+// Awaits four tagged word pairs (p[u], p[u] + 1): loads them all, then re-reads only the words
+// that do not carry the tag yet, all in flight together, until every word carries it or the
+// thread's poll budget is spent. Returns false when the budget ran out.
+__device__ __forceinline__ bool await4(const uint64_t* const (&p)[4], uint32_t tag,
+                                       uint64_t (&w0)[4], uint64_t (&w1)[4]) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    w0[u] = fetch(p[u]);
+    w1[u] = fetch(p[u] + 1);
+  }
+  for (int left = kSpinLimit; left > 0; --left) {
+    bool all = true;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) all = all && tagged(w0[u], tag) && tagged(w1[u], tag);
+    if (all) return true;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (!tagged(w0[u], tag)) w0[u] = fetch(p[u]);
+      if (!tagged(w1[u], tag)) w1[u] = fetch(p[u] + 1);
+    }
+  }
+  return false;
+}
 
 // ---------------------------------------------------------------------------------------------
 // Row access: groups of E consecutive elements, one 128-bit load per group when the rows are
@@ -802,9 +816,8 @@ __device__ void draw_group(const SampleArgs& a, long j) {
   __shared__ float s_zt[64], s_zd[64];
   __shared__ double red[kWaves];
   __shared__ int ired[kWaves];
-  __shared__ int s_n, s_y, s_budget;
+  __shared__ int s_n, s_y;
   uint64_t* stage = reinterpret_cast<uint64_t*>(s_buf);
-  if (threadIdx.x == 0) s_budget = kSpinLimit;
 
   // 1. Wait for every partial of the request (and the draft-token logits) to carry this call's
   //    tag; the words read in the last round are the data. Staged as (offset bits, sum bits).
@@ -812,47 +825,41 @@ __device__ void draw_group(const SampleArgs& a, long j) {
   const int xi = threadIdx.x < (unsigned)k ? a.tokens[(size_t)b * K + threadIdx.x] : -1;
   const bool want_x = xi >= 0 && xi < V;
   const float uni = threadIdx.x < (unsigned)k ? a.uniforms[(size_t)b * K + threadIdx.x] : 0.0f;
-  // A full check reads every partial of the request. When it fails, the group watches a single
-  // word, the partial of the request's last row-stat group (dispatched last), before checking
-  // again, so that waiting does not load the memory system while the stream still runs.
-  const int last_slot = k > 0 ? K + k : 0;
-  const uint64_t* probe = a.stats + (((size_t)b * NR + last_slot) * C + (C - 1)) * 2;
-  for (;;) {
-    bool ok = true;
-    for (int e0 = 0; e0 < nent; e0 += kBlock * 4) {
-      uint64_t wo[4], wsum[4];
+  // Each thread awaits its share of the request's partials (see await4).
+  bool late = false;
+  for (int e0 = 0; e0 < nent; e0 += kBlock * 4) {
+    const uint64_t* p[4];
+    uint64_t wo[4], wsum[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        int e = e0 + u * kBlock + (int)threadIdx.x;
-        e = e < nent ? e : nent - 1;  // clamped: always a valid entry, no branch around the load
-        const int r = e / C, c = e % C;
-        const int slot = r <= k ? r : K + 1 + (r - k - 1);
-        const uint64_t* p = a.stats + (((size_t)b * NR + slot) * C + c) * 2;
-        wo[u] = fetch(p);
-        wsum[u] = fetch(p + 1);
-      }
+    for (int u = 0; u < 4; ++u) {
+      int e = e0 + u * kBlock + (int)threadIdx.x;
+      e = e < nent ? e : nent - 1;  // clamped: always a valid entry
+      const int r = e / C, c = e % C;
+      const int slot = r <= k ? r : K + 1 + (r - k - 1);
+      p[u] = a.stats + (((size_t)b * NR + slot) * C + c) * 2;
+    }
+    late = late || !await4(p, tag, wo, wsum);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = e0 + u * kBlock + (int)threadIdx.x;
-        if (e < nent) {
-          ok = ok && tagged(wo[u], tag) && tagged(wsum[u], tag);
-          stage[e] = ((uint64_t)payload(wo[u]) << 32) | payload(wsum[u]);
-        }
-      }
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + u * kBlock + (int)threadIdx.x;
+      if (e < nent) stage[e] = ((uint64_t)payload(wo[u]) << 32) | payload(wsum[u]);
     }
-    if (want_x) {  // threads 0..k-1: the logits of draft token i in target and draft row i
-      const uint64_t wt = fetch(&a.gath[(size_t)b * 2 * K + threadIdx.x]);
-      const uint64_t wd = fetch(&a.gath[(size_t)b * 2 * K + K + threadIdx.x]);
-      ok = ok && tagged(wt, tag) && tagged(wd, tag);
-      s_zt[threadIdx.x] = __uint_as_float(payload(wt));
-      s_zd[threadIdx.x] = __uint_as_float(payload(wd));
+  }
+  if (want_x) {  // threads 0..k-1: the logits of draft token i in target and draft row i
+    const uint64_t* pt = &a.gath[(size_t)b * 2 * K + threadIdx.x];
+    const uint64_t* pd = &a.gath[(size_t)b * 2 * K + K + threadIdx.x];
+    uint64_t wt = fetch(pt), wd = fetch(pd);
+    for (int left = kSpinLimit; left > 0 && !(tagged(wt, tag) && tagged(wd, tag)); --left) {
+      if (!tagged(wt, tag)) wt = fetch(pt);
+      if (!tagged(wd, tag)) wd = fetch(pd);
     }
-    if (__syncthreads_and(ok)) break;
-    watch(probe, tag, &s_budget);
-    if (s_budget <= 0) {
-      if (threadIdx.x == 0) a.accepted_len[b] = kTimedOut;
-      return;
-    }
+    late = late || !tagged(wt, tag) || !tagged(wd, tag);
+    s_zt[threadIdx.x] = __uint_as_float(payload(wt));
+    s_zd[threadIdx.x] = __uint_as_float(payload(wd));
+  }
+  if (__syncthreads_or(late)) {
+    if (threadIdx.x == 0) a.accepted_len[b] = kTimedOut;
+    return;
   }
 
   // 2. Row normalisers: combine the C partials of each used row in fp64. A row is handled by
@@ -945,18 +952,29 @@ __device__ void draw_group(const SampleArgs& a, long j) {
     publish(&ct[2 * c2 + 1], tag, (uint32_t)bits);
   }
 
-  // 6. Every chunk total of the request, then the chunk holding r * Z (same answer in every
-  //    group of the request). Full check first; when it fails, watch the last chunk's word.
-  for (;;) {
-    bool ok = true;
-    for (int c = threadIdx.x; c < C2; c += kBlock) {
-      const uint64_t hi = fetch(&ct[2 * c]), lo = fetch(&ct[2 * c + 1]);
-      ok = ok && tagged(hi, tag) && tagged(lo, tag);
-      ctot[c] = __longlong_as_double((long long)(((uint64_t)payload(hi) << 32) | payload(lo)));
+  // 6. Every chunk total of the request (awaited as above), then the chunk holding r * Z (same
+  //    answer in every group of the request).
+  {
+    bool late2 = false;
+    for (int c0 = 0; c0 < C2; c0 += kBlock * 4) {
+      const uint64_t* p[4];
+      uint64_t hi[4], lo[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        int c = c0 + u * kBlock + (int)threadIdx.x;
+        c = c < C2 ? c : C2 - 1;
+        p[u] = &ct[2 * c];
+      }
+      late2 = late2 || !await4(p, tag, hi, lo);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + u * kBlock + (int)threadIdx.x;
+        if (c < C2)
+          ctot[c] = __longlong_as_double(
+              (long long)(((uint64_t)payload(hi[u]) << 32) | payload(lo[u])));
+      }
     }
-    if (__syncthreads_and(ok)) break;
-    watch(&ct[2 * (C2 - 1) + 1], tag, &s_budget);
-    if (s_budget <= 0) {
+    if (__syncthreads_or(late2)) {
       if (threadIdx.x == 0) a.accepted_len[b] = kTimedOut;
       return;
     }
@@ -1070,38 +1088,28 @@ __device__ void finish_group(const GreedyArgs& a, int b) {
   const uint32_t tag = a.tag;
   __shared__ uint64_t stage[kStageMax];
   __shared__ int s_g[kMaxK + 1];
-  __shared__ int s_n, s_budget;
-  if (threadIdx.x == 0) s_budget = kSpinLimit;
+  __shared__ int s_n;
   const int nent = (k + 1) * C;  // <= kStageMax by the plan
-  // Full check first; when it fails, watch the partial of the request's last argmax group.
-  const uint64_t* probe = a.gstats + ((size_t)b * NR * C + nent - 1) * 2;
-  for (;;) {
-    bool ok = true;
-    for (int e0 = 0; e0 < nent; e0 += kBlock * 4) {
-      uint64_t wv[4], wi[4];
+  bool late = false;
+  for (int e0 = 0; e0 < nent; e0 += kBlock * 4) {
+    const uint64_t* p[4];
+    uint64_t wv[4], wi[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        int e = e0 + u * kBlock + (int)threadIdx.x;
-        e = e < nent ? e : nent - 1;
-        const uint64_t* p = a.gstats + ((size_t)b * NR * C + e) * 2;  // rows 0..k are first
-        wv[u] = fetch(p);
-        wi[u] = fetch(p + 1);
-      }
+    for (int u = 0; u < 4; ++u) {
+      int e = e0 + u * kBlock + (int)threadIdx.x;
+      e = e < nent ? e : nent - 1;
+      p[u] = a.gstats + ((size_t)b * NR * C + e) * 2;  // rows 0..k come first
+    }
+    late = late || !await4(p, tag, wv, wi);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = e0 + u * kBlock + (int)threadIdx.x;
-        if (e < nent) {
-          ok = ok && tagged(wv[u], tag) && tagged(wi[u], tag);
-          stage[e] = ((uint64_t)payload(wv[u]) << 32) | payload(wi[u]);
-        }
-      }
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + u * kBlock + (int)threadIdx.x;
+      if (e < nent) stage[e] = ((uint64_t)payload(wv[u]) << 32) | payload(wi[u]);
     }
-    if (__syncthreads_and(ok)) break;
-    watch(probe, tag, &s_budget);
-    if (s_budget <= 0) {
-      if (threadIdx.x == 0) a.accepted_len[b] = kTimedOut;
-      return;
-    }
+  }
+  if (__syncthreads_or(late)) {
+    if (threadIdx.x == 0) a.accepted_len[b] = kTimedOut;
+    return;
   }
   for (int i = threadIdx.x; i <= k; i += kBlock) {
     float v = -INFINITY;
