@@ -62,8 +62,10 @@ constexpr int kTileUnroll = 4;    // draw tiles in flight per wave
 constexpr int kStageMax = 2048;   // partials of one request staged in LDS: (2K+1)*C, (K+1)*Cg
 constexpr int kChunkTiles = 512;  // draw tiles per draw group, at most
 constexpr int kMaxC2 = 512;       // draw groups per request, at most
+constexpr int kDrawGroups = 1024;  // draw groups per launch the plan aims at
 constexpr int kSpinLimit = 1 << 21;  // polls (about 1 us each) before a waiting group gives up
 constexpr int32_t kTimedOut = -2;    // accepted_len value reported by a group that gave up
+constexpr int kPollSleep = 2;        // s_sleep units (64 clocks each) between two polls
 
 // ---------------------------------------------------------------------------------------------
 // Work decomposition (host side, shared by the workspace query and the launches).
@@ -88,10 +90,14 @@ Plan make_plan(int B, int K, int V) {
   Plan p;
   p.C = chunks_for((long)B * (2 * K + 1), V, 8192, 4096, kStageMax / (2 * K + 1));
   p.NT = (V + kTile - 1) / kTile;
-  // About 1024 draw groups in all, so that every one of them is resident once the row-stat
-  // groups drain (more queue behind each other and delay the last requests' draws); at least
-  // 4 tiles (one per wave) per group.
-  p.C2 = chunks_for(B, p.NT, 1024, 4, kMaxC2);
+  // About kDrawGroups draw groups in all, so that every one of them is resident once the
+  // row-stat groups drain (more queue behind each other and delay the last requests' draws);
+  // at least 4 tiles (one per wave) per group.
+  p.C2 = chunks_for(B, p.NT, kDrawGroups, 4, kMaxC2);
+  // At most kWaves * kTileUnroll tiles per group, so that each wave loads its tiles in one
+  // round, unless that would more than double the draw groups.
+  const long one_round = (p.NT + kWaves * kTileUnroll - 1) / (kWaves * kTileUnroll);
+  if (p.C2 < one_round && (long)B * one_round <= 2L * kDrawGroups) p.C2 = (int)one_round;
   const int need = (p.NT + kChunkTiles - 1) / kChunkTiles;
   if (p.C2 < need) p.C2 = need;
   p.Cg = chunks_for((long)B * (K + 1), V, 8192, 4096, kStageMax / (K + 1));
@@ -109,7 +115,7 @@ struct DrawParams {
 
 struct Layout {
   size_t stats;   // uint64 [B][2K+1][C][2]  row-stat partials: tagged offset, tagged sum
-  size_t gath;    // uint64 [B][2K]          tagged logit at the draft token: target i, draft K+i
+  size_t gath;    // uint64 [B][K][2]        tagged logits at draft token i: target row, draft row
   size_t ctot;    // uint64 [B][C2][2]       tagged draw chunk totals (fp64 high, low halves)
   size_t gstats;  // uint64 [B][K+1][Cg][2]  greedy partials: tagged value, tagged index
   size_t total;
@@ -146,21 +152,93 @@ __device__ __forceinline__ bool tagged(uint64_t w, uint32_t tag) { return (uint3
 
 __device__ __forceinline__ uint32_t payload(uint64_t w) { return (uint32_t)w; }
 
-// Awaits four tagged word pairs (p[u], p[u] + 1): loads them all, then re-reads only the words
-// that do not carry the tag yet, all in flight together, until every word carries it or the
-// thread's poll budget is spent. Returns false when the budget ran out.
-__device__ __forceinline__ bool await4(const uint64_t* const (&p)[4], uint32_t tag,
-                                       uint64_t (&w0)[4], uint64_t (&w1)[4]) {
+// ---------------------------------------------------------------------------------------------
+// Wave primitives on DPP: cross-lane moves done inside the vector ALU, without the LDS round trip
+// of a lane permute. A scan combines each lane with the lanes 1, 2, 4 and 8 below it inside its
+// row of 16 lanes, then adds lane 15 of each row into the next row and lane 31 into rows 2 and 3,
+// so lane l ends up holding the combination of lanes 0..l (lane 63: the whole wave). A source
+// lane outside the row, or a row that the mask leaves out, reads the identity. Every scan runs
+// with the whole wave active.
+
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppWaveShr1 = 0x138, kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x, uint32_t identity) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)x, CTRL, ROWS, 0xf, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_f32(float x, float identity) {
+  return __uint_as_float(dpp_u32<CTRL, ROWS>(__float_as_uint(x), __float_as_uint(identity)));
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_f64(double x) {  // identity 0.0
+  const uint64_t v = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = dpp_u32<CTRL, ROWS>((uint32_t)v, 0u);
+  const uint32_t hi = dpp_u32<CTRL, ROWS>((uint32_t)(v >> 32), 0u);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Value of lane l (l wave-uniform), as a wave-uniform value.
+__device__ __forceinline__ uint32_t lane_u32(uint32_t x, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, l);
+}
+__device__ __forceinline__ float lane_f32(float x, int l) {
+  return __uint_as_float(lane_u32(__float_as_uint(x), l));
+}
+__device__ __forceinline__ double lane_f64(double x, int l) {
+  const uint64_t v = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = lane_u32((uint32_t)v, l), hi = lane_u32((uint32_t)(v >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Applies one scan step to the state of every lane: f(state, state of the source lane).
+#define SV_SCAN_STEPS(STEP)   \
+  STEP(kDppRowShr1, 0xf);     \
+  STEP(kDppRowShr2, 0xf);     \
+  STEP(kDppRowShr4, 0xf);     \
+  STEP(kDppRowShr8, 0xf);     \
+  STEP(kDppRowBcast15, 0xa);  \
+  STEP(kDppRowBcast31, 0xc)
+
+// Inclusive prefix sum of one fp64 value per lane.
+__device__ __forceinline__ double wave_scan_f64(double x) {
+#define SV_ADD_STEP(CTRL, ROWS) x += dpp_f64<CTRL, ROWS>(x)
+  SV_SCAN_STEPS(SV_ADD_STEP);
+#undef SV_ADD_STEP
+  return x;
+}
+
+// Sum over the wave, wave-uniform.
+__device__ __forceinline__ double wave_sum_f64(double x) { return lane_f64(wave_scan_f64(x), 63); }
+
+// Maximum over the wave, wave-uniform.
+__device__ __forceinline__ int wave_max_i32(int x) {
+#define SV_MAX_STEP(CTRL, ROWS) x = max(x, (int)dpp_u32<CTRL, ROWS>((uint32_t)x, (uint32_t)INT_MIN))
+  SV_SCAN_STEPS(SV_MAX_STEP);
+#undef SV_MAX_STEP
+  return (int)lane_u32((uint32_t)x, 63);
+}
+
+// Awaits up to four tagged word pairs (p[u], p[u] + 1), those with live[u]: loads them all, then
+// re-reads only the words that do not carry the tag yet, all in flight together, until every
+// word carries it or the thread's poll budget is spent. Between two polls the wave sleeps
+// kPollSleep units, which keeps waiting groups from flooding the memory system with requests
+// while other groups stream. Returns false when the budget ran out.
+__device__ __forceinline__ bool await4(const uint64_t* const (&p)[4], const bool (&live)[4],
+                                       uint32_t tag, uint64_t (&w0)[4], uint64_t (&w1)[4]) {
+  const uint64_t done = (uint64_t)tag << 32;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    w0[u] = fetch(p[u]);
-    w1[u] = fetch(p[u] + 1);
+    w0[u] = live[u] ? fetch(p[u]) : done;
+    w1[u] = live[u] ? fetch(p[u] + 1) : done;
   }
   for (int left = kSpinLimit; left > 0; --left) {
     bool all = true;
 #pragma unroll
     for (int u = 0; u < 4; ++u) all = all && tagged(w0[u], tag) && tagged(w1[u], tag);
     if (all) return true;
+    if (kPollSleep > 0) __builtin_amdgcn_s_sleep(kPollSleep);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if (!tagged(w0[u], tag)) w0[u] = fetch(p[u]);
@@ -340,6 +418,16 @@ __device__ __forceinline__ void merge_stats(float& o, float& s, float o2, float 
   o = on;
 }
 
+// (offset, sum) partials of the whole wave merged, wave-uniform.
+__device__ __forceinline__ void wave_merge_stats(float& o, float& s) {
+#define SV_STATS_STEP(CTRL, ROWS) \
+  merge_stats(o, s, dpp_f32<CTRL, ROWS>(o, -FLT_MAX), dpp_f32<CTRL, ROWS>(s, 0.0f))
+  SV_SCAN_STEPS(SV_STATS_STEP);
+#undef SV_STATS_STEP
+  o = lane_f32(o, 63);
+  s = lane_f32(s, 63);
+}
+
 // Online softmax statistics: o is an integer >= c * max(z) seen so far, s0 + s1 is the sum of
 // 2^(fma(z, c, -o)). The offset moves once per round of N groups, not per element.
 template <int E>
@@ -404,7 +492,7 @@ struct SampleArgs {
   long n_stat_groups;  // B * (2K+1) * C: groups before this index are row-stat groups
   uint32_t tag;        // this call's tag
   uint64_t* stats;
-  uint64_t* gath;
+  uint64_t* gath;  // [B][K][2]
   uint64_t* ctot;
   int32_t* accepted_len;
   int32_t* committed;
@@ -415,8 +503,8 @@ struct SampleArgs {
 // Row-stat group wg = (b * (2K+1) + slot) * C + c. Row slot s <= K is target row s, slot K+1+d
 // is draft row d. Unused rows (s > k_b, d >= k_b) return at once without a read.
 // Publishes stats[b][s][c] = (o, sum) with sum = sum_v 2^(fma(z_v, c32, -o)), and, for target
-// slots i < k_b and draft slots d < k_b, the group whose chunk holds the draft token publishes
-// its logit in gath[b][i] (target) or gath[b][K+d] (draft).
+// slots i < k_b and draft slots i < k_b, the group whose chunk holds the draft token x_i
+// publishes its logit in gath[b][i][0] (target row i) or gath[b][i][1] (draft row i).
 template <typename T, bool VEC>
 __device__ void row_stat_group(const SampleArgs& a, long wg) {
   constexpr int E = Rows<T, VEC>::E;
@@ -429,27 +517,30 @@ __device__ void row_stat_group(const SampleArgs& a, long wg) {
   const int k = clamp_k(a.num_draft, b, K);
   const T* row;
   int tslot;  // draft slot whose logit this row provides, or -1 (the extra-draw row)
-  int gidx;   // where that logit goes in gath
+  int gidx;   // 0: the logit is a target logit, 1: a draft logit
   if (slot <= K) {
     if (slot > k) return;
     row = static_cast<const T*>(a.target) + ((size_t)b * (K + 1) + slot) * (size_t)V;
     tslot = slot < k ? slot : -1;
-    gidx = slot;
+    gidx = 0;
   } else {
     const int d = slot - K - 1;
     if (d >= k) return;
     row = static_cast<const T*>(a.draft) + ((size_t)b * K + d) * (size_t)V;
     tslot = d;
-    gidx = K + d;
+    gidx = 1;
   }
   const int G = VEC ? V / E : V;
   const int g0 = (int)((long)G * c / C), g1 = (int)((long)G * (c + 1) / C);
 
   if (threadIdx.x == 0 && tslot >= 0) {
+    // a token outside the vocabulary has no logit: chunk 0 publishes a placeholder instead, so
+    // that the word of every slot below k_b is published
     const int x = a.tokens[(size_t)b * K + tslot];
-    if (x >= 0 && x < V && x >= g0 * E && x < g1 * E)
-      publish(&a.gath[(size_t)b * 2 * K + gidx], a.tag,
-              __float_as_uint(Rows<T, VEC>::at(row, x)));
+    const bool valid = x >= 0 && x < V;
+    if (valid ? (x >= g0 * E && x < g1 * E) : c == 0)
+      publish(&a.gath[((size_t)b * K + tslot) * 2 + gidx], a.tag,
+              valid ? __float_as_uint(Rows<T, VEC>::at(row, x)) : 0u);
   }
 
   SoftmaxAcc<E> acc{a.c32, -FLT_MAX, 0.0f, 0.0f};
@@ -457,12 +548,7 @@ __device__ void row_stat_group(const SampleArgs& a, long wg) {
   float o = acc.o, s = acc.s0 + acc.s1;
 
   // wave reduce, then across the 4 waves through LDS
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const float o2 = __shfl_xor(o, m);
-    const float s2 = __shfl_xor(s, m);
-    merge_stats(o, s, o2, s2);
-  }
+  wave_merge_stats(o, s);
   __shared__ float so[kWaves], ss[kWaves];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) {
@@ -543,74 +629,51 @@ struct TileRows {
   }
 };
 
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
-}
+// Staged row-stat entry that merges as nothing: offset -FLT_MAX, sum 0.
+constexpr uint64_t kEmptyStat = (uint64_t)0xff7fffffu << 32;
 
-__device__ __forceinline__ double wave_incl_scan_f64(double v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const double u = __shfl_up(v, d);
-    if (lane >= d) v += u;
+// Merge of a chunk partial (o2, s2) into a row normaliser (O, S) in fp64. Offsets are integers,
+// so rescaling by 2^(o - O) is exact and the result does not depend on the order in which
+// larger offsets arrive (up to the order of the additions).
+__device__ __forceinline__ void merge_stats_f64(float& O, double& S, float o2, double s2) {
+  if (o2 > O) {
+    float d = O - o2;
+    d = d < -2000.0f ? -2000.0f : d;
+    S = ldexp(S, (int)d) + s2;
+    O = o2;
+  } else {
+    float d = o2 - O;
+    d = d < -2000.0f ? -2000.0f : d;
+    S += ldexp(s2, (int)d);
   }
-  return v;
 }
 
-__device__ __forceinline__ int wave_min_i32(int v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = min(v, __shfl_xor(v, m));
-  return v;
+// Merges the (O, S) pairs of aligned groups of RL lanes (RL a power of two, at most 64); every
+// lane of a group ends with the group's pair. Pairs of lanes exchange through DPP (quad
+// permutations, then the half-row and row mirrors, which pair the already merged quads and
+// half-rows), and through lane permutes across rows.
+__device__ __forceinline__ void merge_pair_f64(float& O, double& S, float o2, double s2) {
+  const float on = fmaxf(O, o2);
+  float d1 = O - on, d2 = o2 - on;
+  d1 = d1 < -2000.0f ? -2000.0f : d1;
+  d2 = d2 < -2000.0f ? -2000.0f : d2;
+  S = ldexp(S, (int)d1) + ldexp(s2, (int)d2);  // the same sum in both lanes of a pair
+  O = on;
 }
-
-__device__ __forceinline__ int wave_max_i32(int v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = max(v, __shfl_xor(v, m));
-  return v;
-}
-
-__device__ __forceinline__ double block_sum_f64(double v, double* red) {
-  v = wave_sum_f64(v);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  double t = 0.0;
-  for (int i = 0; i < kWaves; ++i) t += red[i];
-  return t;  // every thread gets the same total (same order of additions)
-}
-
-// Inclusive block scan of one fp64 value per thread; *total receives the block total.
-__device__ __forceinline__ double block_scan_f64(double v, double* red, double* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  v = wave_incl_scan_f64(v, lane);
-  __syncthreads();
-  if (lane == 63) red[wave] = v;
-  __syncthreads();
-  double before = 0.0, all = 0.0;
-  for (int i = 0; i < kWaves; ++i) {
-    if (i < wave) before += red[i];
-    all += red[i];
-  }
-  *total = all;
-  return before + v;
-}
-
-__device__ __forceinline__ int block_min_i32(int v, int* red) {
-  v = wave_min_i32(v);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  int t = red[0];
-  for (int i = 1; i < kWaves; ++i) t = min(t, red[i]);
-  return t;
+__device__ __forceinline__ void merge_row_lanes(float& O, double& S, int RL) {
+  if (RL >= 2) merge_pair_f64(O, S, dpp_f32<0xB1, 0xf>(O, 0.0f), dpp_f64<0xB1, 0xf>(S));  // l^1
+  if (RL >= 4) merge_pair_f64(O, S, dpp_f32<0x4E, 0xf>(O, 0.0f), dpp_f64<0x4E, 0xf>(S));  // l^2
+  if (RL >= 8) merge_pair_f64(O, S, dpp_f32<0x141, 0xf>(O, 0.0f), dpp_f64<0x141, 0xf>(S));
+  if (RL >= 16) merge_pair_f64(O, S, dpp_f32<0x140, 0xf>(O, 0.0f), dpp_f64<0x140, 0xf>(S));
+  if (RL >= 32) merge_pair_f64(O, S, __shfl_xor(O, 16), __shfl_xor(S, 16));
+  if (RL >= 64) merge_pair_f64(O, S, __shfl_xor(O, 32), __shfl_xor(S, 32));
 }
 
 // One wave: inverse CDF inside tile t. Returns the first element v of the tile whose running sum
 // (from the start of the tile, element order) exceeds `target`; if none does (rounding), the last
-// element of the tile with positive weight; -1 if the tile has none.
+// element of the tile with positive weight; -1 if the tile has none. Sub-tile j is scanned over
+// the lanes (fp64 lane sums in element order, then a wave prefix sum); the first lane whose
+// prefix passes the target walks its own elements.
 template <typename T, bool VEC, bool RESID>
 __device__ int tile_find(const T* rt, const T* rd, const DrawParams& w, float c32, int G, int t,
                          double target) {
@@ -632,19 +695,24 @@ __device__ int tile_find(const T* rt, const T* rd, const DrawParams& w, float c3
       mine += (double)v[e];
       if (v[e] > 0.0f) last_pos = first + e;
     }
-    const double incl = wave_incl_scan_f64(mine, lane);
-    int cand = INT_MAX;
-    if (base + incl > target) {
-      double run = base + (incl - mine);
+    const double incl = wave_scan_f64(mine);
+    const double excl = dpp_f64<kDppWaveShr1, 0xf>(incl);  // exactly the previous lane's prefix
+    const uint64_t hit = __ballot(base + incl > target);
+    if (hit) {
+      const int L = __ffsll((long long)hit) - 1;
+      int cand = INT_MAX;
+      if (lane == L) {
+        double run = base + excl;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        run += (double)v[e];
-        if (cand == INT_MAX && run > target) cand = first + e;
+        for (int e = 0; e < E; ++e) {
+          run += (double)v[e];
+          if (cand == INT_MAX && v[e] > 0.0f && run > target) cand = first + e;
+        }
       }
+      cand = (int)lane_u32((uint32_t)cand, L);
+      if (cand != INT_MAX) return cand;
     }
-    const int found = wave_min_i32(cand);
-    if (found != INT_MAX) return found;
-    base += __shfl(incl, 63);
+    base += lane_f64(incl, 63);
   }
   return wave_max_i32(last_pos);
 }
@@ -677,98 +745,79 @@ __device__ __forceinline__ void tile_sums(const T* rt, const T* rd, const DrawPa
 struct Pick {
   int idx;       // chosen index; -1 when the total is 0
   bool found;    // false: no prefix exceeded the target (rounding); idx = last positive entry
-  double rel;    // target minus the sum of the entries before idx
+  double rel;    // target minus the sum of the entries before idx (infinite when not found)
   double total;  // sum of all n entries
 };
 
-// Inverse CDF over n fp64 weights in LDS, block-wide, in index order: the first index whose
-// inclusive prefix exceeds the target. The target is frac * total when frac >= 0, else `fixed`.
-// Sums run in blocks of kBlock entries with fp64 block scans in a fixed order, so every group
+// Inverse CDF over n fp64 weights in LDS, by one wave, in index order: the first index with a
+// positive weight whose inclusive prefix exceeds the target, which is frac * total when
+// frac >= 0, else `fixed`. Lane l sums the block [l*m, (l+1)*m) (m = ceil(n/64)) in index order,
+// a wave prefix sum over the block sums gives each block's starting prefix, and the first lane
+// whose prefix passes the target walks its block. The result is wave-uniform, and every wave
 // that runs it on the same values gets the same answer.
-__device__ Pick lds_pick(const double* vals, int n, double frac, double fixed, double* red,
-                         int* ired) {
-  __shared__ double s_rel;
-  Pick p;
-  if (n <= kBlock) {  // one block scan gives the total and every prefix
-    const int i = (int)threadIdx.x;
-    const double v = i < n ? vals[i] : 0.0;
-    double total;
-    const double incl = block_scan_f64(v, red, &total);
-    p.total = total;
-    p.rel = 0.0;
-    if (!(total > 0.0)) {
-      p.idx = -1;
-      p.found = false;
-      return p;
-    }
-    const double target = frac >= 0.0 ? frac * total : fixed;
-    const int cand = (i < n && v > 0.0 && incl > target) ? i : INT_MAX;
-    const int found = block_min_i32(cand, ired);
-    if (found != INT_MAX) {
-      if (i == found) s_rel = target - (incl - v);
-      __syncthreads();
-      p.idx = found;
-      p.found = true;
-      p.rel = s_rel;
-      return p;
-    }
-    p.idx = -block_min_i32(-(i < n && v > 0.0 ? i : -1), ired);
-    p.found = false;
-    p.rel = INFINITY;
-    return p;
-  }
-  double total = 0.0;
-  for (int i0 = 0; i0 < n; i0 += kBlock) {
-    const int i = i0 + (int)threadIdx.x;
-    double tot;
-    block_scan_f64(i < n ? vals[i] : 0.0, red, &tot);
-    total += tot;
-  }
-  p.total = total;
-  p.rel = 0.0;
-  if (!(total > 0.0)) {
-    p.idx = -1;
-    p.found = false;
-    return p;
-  }
-  const double target = frac >= 0.0 ? frac * total : fixed;
-  double base = 0.0;
+__device__ Pick wave_pick(const double* vals, int n, double frac, double fixed) {
+  const int lane = threadIdx.x & 63;
+  const int m = (n + 63) >> 6;
+  const int i0 = min(n, lane * m), i1 = min(n, i0 + m);
+  double blk = 0.0;
   int last_pos = -1;
-  for (int i0 = 0; i0 < n; i0 += kBlock) {
-    const int i = i0 + (int)threadIdx.x;
-    const double v = i < n ? vals[i] : 0.0;
+  for (int i = i0; i < i1; ++i) {
+    const double v = vals[i];
+    blk += v;
     if (v > 0.0) last_pos = i;
-    double tot;
-    const double incl = block_scan_f64(v, red, &tot);
-    const int cand = (i < n && v > 0.0 && base + incl > target) ? i : INT_MAX;
-    const int found = block_min_i32(cand, ired);
-    if (found != INT_MAX) {
-      if (i == found) s_rel = target - (base + (incl - v));
-      __syncthreads();
-      p.idx = found;
-      p.found = true;
-      p.rel = s_rel;
-      return p;
-    }
-    base += tot;
   }
-  p.idx = -block_min_i32(-last_pos, ired);
+  const double incl = wave_scan_f64(blk);
+  const double excl = dpp_f64<kDppWaveShr1, 0xf>(incl);
+  Pick p;
+  p.total = lane_f64(incl, 63);
+  p.idx = -1;
   p.found = false;
   p.rel = INFINITY;
+  if (!(p.total > 0.0)) return p;
+  const double target = frac >= 0.0 ? frac * p.total : fixed;
+  const uint64_t hit = __ballot(incl > target);
+  if (hit) {
+    const int L = __ffsll((long long)hit) - 1;
+    int idx = -1;
+    double rel = 0.0;
+    if (lane == L) {
+      double run = excl;
+      for (int i = i0; i < i1; ++i) {
+        const double v = vals[i];
+        const double nx = run + v;
+        if (v > 0.0 && nx > target) {
+          idx = i;
+          rel = target - run;
+          break;
+        }
+        run = nx;
+      }
+    }
+    idx = (int)lane_u32((uint32_t)idx, L);
+    if (idx >= 0) {
+      p.idx = idx;
+      p.found = true;
+      p.rel = lane_f64(rel, L);
+      return p;
+    }
+  }
+  p.idx = wave_max_i32(last_pos);
   return p;
 }
 
 // Zero residual mass at a rejected slot (possible only through fp32 rounding): draw from p_n
-// over the whole row instead, with one group, in blocks of kChunkTiles tiles (two passes).
+// over the whole row instead, with one group, in blocks of kChunkTiles tiles (two passes). Every
+// wave runs the picks on the same tile sums, so all waves take the same branches. Returns the
+// token (wave 0 only; -1 if the row has no positive weight).
 template <typename T, bool VEC>
 __device__ int full_row_draw(const T* rt, const DrawParams& w, float c32, int G, int NT,
-                             double r, double* tsum, double* red, int* ired) {
+                             double r, double* tsum) {
   double total = 0.0;
   for (int t0 = 0; t0 < NT; t0 += kChunkTiles) {
     const int t1 = min(NT, t0 + kChunkTiles);
     tile_sums<T, VEC, false>(rt, rt, w, c32, G, t0, t1, tsum);
     __syncthreads();
-    total += lds_pick(tsum, t1 - t0, -1.0, INFINITY, red, ired).total;
+    total += wave_pick(tsum, t1 - t0, -1.0, INFINITY).total;
     __syncthreads();
   }
   const double target = r * total;
@@ -779,7 +828,7 @@ __device__ int full_row_draw(const T* rt, const DrawParams& w, float c32, int G,
     const int t1 = min(NT, t0 + kChunkTiles);
     tile_sums<T, VEC, false>(rt, rt, w, c32, G, t0, t1, tsum);
     __syncthreads();
-    const Pick p = lds_pick(tsum, t1 - t0, -1.0, target - acc, red, ired);
+    const Pick p = wave_pick(tsum, t1 - t0, -1.0, target - acc);
     __syncthreads();
     if (p.found) {
       tile = t0 + p.idx;
@@ -789,13 +838,9 @@ __device__ int full_row_draw(const T* rt, const DrawParams& w, float c32, int G,
     if (p.idx >= 0) tile = t0 + p.idx;  // last tile with mass so far, drawn past its end
     acc += p.total;
   }
-  __shared__ int s_y;
-  if (threadIdx.x < 64) {
-    const int y = tile >= 0 ? tile_find<T, VEC, false>(rt, rt, w, c32, G, tile, rel) : -1;
-    if (threadIdx.x == 0) s_y = y;
-  }
-  __syncthreads();
-  return s_y;
+  int y = -1;
+  if (threadIdx.x < 64 && tile >= 0) y = tile_find<T, VEC, false>(rt, rt, w, c32, G, tile, rel);
+  return y;
 }
 
 // Draw group j = b * C2 + c2; chunk c2 covers tiles [NT*c2/C2, NT*(c2+1)/C2).
@@ -808,84 +853,91 @@ __device__ void draw_group(const SampleArgs& a, long j) {
   const int k = clamp_k(a.num_draft, b, K);
   const float c32 = a.c32;
   const uint32_t tag = a.tag;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
   // s_buf first stages the row-stat partials, then holds tile sums and chunk totals.
   __shared__ double s_buf[kStageMax];
   __shared__ float s_o[2 * kMaxK + 1];
   __shared__ double s_S[2 * kMaxK + 1];
-  __shared__ float s_zt[64], s_zd[64];
-  __shared__ double red[kWaves];
-  __shared__ int ired[kWaves];
-  __shared__ int s_n, s_y;
+  __shared__ float s_zt[kMaxK], s_zd[kMaxK];
   uint64_t* stage = reinterpret_cast<uint64_t*>(s_buf);
 
-  // 1. Wait for every partial of the request (and the draft-token logits) to carry this call's
-  //    tag; the words read in the last round are the data. Staged as (offset bits, sum bits).
-  const int nrow = 2 * k + 1, nent = nrow * C;  // nent <= kStageMax by the plan
-  const int xi = threadIdx.x < (unsigned)k ? a.tokens[(size_t)b * K + threadIdx.x] : -1;
+  // Per-request inputs, read before the wait. Lane i < k of every wave holds slot i.
+  const double r = (double)a.residual[b];
+  const int xi = lane < k ? a.tokens[(size_t)b * K + lane] : -1;
+  const float uni = lane < k ? a.uniforms[(size_t)b * K + lane] : 0.0f;
   const bool want_x = xi >= 0 && xi < V;
-  const float uni = threadIdx.x < (unsigned)k ? a.uniforms[(size_t)b * K + threadIdx.x] : 0.0f;
-  // Each thread awaits its share of the request's partials (see await4).
+
+  // 1. Wait for every partial of the request and the logits at the draft tokens to carry this
+  //    call's tag; the words read in the last round are the data. Entries e < nent are
+  //    row-stat partials (staged as offset bits, sum bits), entries nent + i the two logits of
+  //    draft token i.
+  const int nrow = 2 * k + 1, nent = nrow * C;  // nent <= kStageMax by the plan
+  const int ntot = nent + k;
   bool late = false;
-  for (int e0 = 0; e0 < nent; e0 += kBlock * 4) {
+  for (int e0 = 0; e0 < ntot; e0 += kBlock * 4) {
     const uint64_t* p[4];
-    uint64_t wo[4], wsum[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      int e = e0 + u * kBlock + (int)threadIdx.x;
-      e = e < nent ? e : nent - 1;  // clamped: always a valid entry
-      const int r = e / C, c = e % C;
-      const int slot = r <= k ? r : K + 1 + (r - k - 1);
-      p[u] = a.stats + (((size_t)b * NR + slot) * C + c) * 2;
-    }
-    late = late || !await4(p, tag, wo, wsum);
+    bool live[4];
+    uint64_t w0[4], w1[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int e = e0 + u * kBlock + (int)threadIdx.x;
-      if (e < nent) stage[e] = ((uint64_t)payload(wo[u]) << 32) | payload(wsum[u]);
+      live[u] = e < ntot;
+      if (e < nent) {
+        const int r_ = e / C, c = e % C;
+        const int slot = r_ <= k ? r_ : K + 1 + (r_ - k - 1);
+        p[u] = a.stats + (((size_t)b * NR + slot) * C + c) * 2;
+      } else {
+        const int i = live[u] ? e - nent : 0;
+        p[u] = a.gath + ((size_t)b * K + i) * 2;
+      }
     }
-  }
-  if (want_x) {  // threads 0..k-1: the logits of draft token i in target and draft row i
-    const uint64_t* pt = &a.gath[(size_t)b * 2 * K + threadIdx.x];
-    const uint64_t* pd = &a.gath[(size_t)b * 2 * K + K + threadIdx.x];
-    uint64_t wt = fetch(pt), wd = fetch(pd);
-    for (int left = kSpinLimit; left > 0 && !(tagged(wt, tag) && tagged(wd, tag)); --left) {
-      if (!tagged(wt, tag)) wt = fetch(pt);
-      if (!tagged(wd, tag)) wd = fetch(pd);
+    late = late || !await4(p, live, tag, w0, w1);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + u * kBlock + (int)threadIdx.x;
+      if (e < nent) {
+        stage[e] = ((uint64_t)payload(w0[u]) << 32) | payload(w1[u]);
+      } else if (e < ntot) {
+        s_zt[e - nent] = __uint_as_float(payload(w0[u]));
+        s_zd[e - nent] = __uint_as_float(payload(w1[u]));
+      }
     }
-    late = late || !tagged(wt, tag) || !tagged(wd, tag);
-    s_zt[threadIdx.x] = __uint_as_float(payload(wt));
-    s_zd[threadIdx.x] = __uint_as_float(payload(wd));
   }
   if (__syncthreads_or(late)) {
     if (threadIdx.x == 0) a.accepted_len[b] = kTimedOut;
     return;
   }
 
-  // 2. Row normalisers: combine the C partials of each used row in fp64. A row is handled by
-  //    L = pow2ceil(C) lanes (at most 64), each lane taking chunks lane, lane + L, ...; maximum
-  //    and sum go through a fixed shuffle tree.
+  // 2. Row normalisers: the C partials of each used row combined in fp64. Row r is handled by
+  //    RL lanes (RL = 1 unless C > 16), lane li taking chunks li, li + RL, ... in order, eight
+  //    LDS reads in flight at a time; the RL lanes of a row then merge their (O, S) pairs.
   {
-    int L = 1;
-    while (L < C && L < 64) L <<= 1;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int sub = lane / L, li = lane % L, per_wave = 64 / L;
-    for (int r0 = wave * per_wave; r0 < nrow; r0 += kWaves * per_wave) {
-      const int r = r0 + sub;
-      const bool live = r < nrow;
-      const uint64_t* st = stage + (live ? r : 0) * C;
+    int RL = 1;
+    while (RL * 16 < C) RL <<= 1;  // C <= kStageMax, so RL <= 128: capped below
+    RL = RL > 64 ? 64 : RL;
+    for (int t0 = 0; t0 < nrow * RL; t0 += kBlock) {
+      const int t = t0 + (int)threadIdx.x;
+      const int row = t / RL, li = t % RL;
+      const bool live = row < nrow;
+      const uint64_t* st = stage + (live ? row : 0) * C;
       float O = -FLT_MAX;
-      for (int c = li; c < C; c += L) O = fmaxf(O, __uint_as_float((uint32_t)(st[c] >> 32)));
-      for (int m = L >> 1; m >= 1; m >>= 1) O = fmaxf(O, __shfl_xor(O, m));
       double S = 0.0;
-      for (int c = li; c < C; c += L) {
-        float d = __uint_as_float((uint32_t)(st[c] >> 32)) - O;
-        d = d < -2000.0f ? -2000.0f : d;
-        S += ldexp((double)__uint_as_float((uint32_t)st[c]), (int)d);
+      for (int c0 = li; c0 < C; c0 += 8 * RL) {
+        uint64_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int c = c0 + u * RL;
+          v[u] = c < C ? st[c] : kEmptyStat;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          merge_stats_f64(O, S, __uint_as_float((uint32_t)(v[u] >> 32)),
+                          (double)__uint_as_float((uint32_t)v[u]));
       }
-      for (int m = L >> 1; m >= 1; m >>= 1) S += __shfl_xor(S, m);
+      if (RL > 1) merge_row_lanes(O, S, RL);
       if (live && li == 0) {
-        const int slot = r <= k ? r : K + 1 + (r - k - 1);
+        const int slot = row <= k ? row : K + 1 + (row - k - 1);
         s_o[slot] = O;
         s_S[slot] = S;
       }
@@ -893,29 +945,28 @@ __device__ void draw_group(const SampleArgs& a, long j) {
   }
   __syncthreads();
 
-  // 3. p(x), q(x), accept decisions and the first rejection (slots 0..k-1 live in wave 0).
-  if (threadIdx.x < 64) {
-    const int i = threadIdx.x;
+  // 3. p(x), q(x), the accept decisions and the first rejection n, in every wave (lane i holds
+  //    slot i), so that n is known to each wave without another barrier.
+  int n;
+  {
     double p = 0.0, q = 0.0;
     bool rej = false;
-    if (i < k) {
+    if (lane < k) {
       if (want_x) {
-        p = exp2((double)s_zt[i] * (double)c32 - (double)s_o[i]) / s_S[i];
-        q = exp2((double)s_zd[i] * (double)c32 - (double)s_o[K + 1 + i]) / s_S[K + 1 + i];
+        p = exp2((double)s_zt[lane] * (double)c32 - (double)s_o[lane]) / s_S[lane];
+        q = exp2((double)s_zd[lane] * (double)c32 - (double)s_o[K + 1 + lane]) /
+            s_S[K + 1 + lane];
       }
       const double t = q > 0.0 ? fmin(1.0, p / q) : (p > 0.0 ? 1.0 : 0.0);
       rej = !((double)uni < t);
     }
-    const unsigned long long m = __ballot(rej);
-    const int n = m ? (__ffsll((long long)m) - 1) : k;
-    if (i == 0) s_n = n;
-    if (c2 == 0 && i < K) {
-      a.target_prob[(size_t)b * K + i] = (float)p;
-      if (a.draft_prob != nullptr) a.draft_prob[(size_t)b * K + i] = (float)q;
+    const uint64_t m = __ballot(rej);
+    n = m ? (__ffsll((long long)m) - 1) : k;
+    if (c2 == 0 && wave == 0 && lane < K) {  // slots k..K-1 get 0
+      a.target_prob[(size_t)b * K + lane] = (float)p;
+      if (a.draft_prob != nullptr) a.draft_prob[(size_t)b * K + lane] = (float)q;
     }
   }
-  __syncthreads();
-  const int n = s_n;
 
   // 4. The draw row: target row n, minus draft row n when slot n was rejected.
   const bool resid = n < k;
@@ -937,35 +988,40 @@ __device__ void draw_group(const SampleArgs& a, long j) {
   const T* rd = resid ? static_cast<const T*>(a.draft) + ((size_t)b * K + n) * (size_t)V : rt;
   const int G = VEC ? V / E : V;
 
-  // 5. Tile sums of this chunk (LDS), and the chunk total for the other groups of the request.
-  double* tsum = s_buf;              // [kChunkTiles]
+  // 5. Tile sums of this chunk (LDS); wave 0 publishes the chunk total for the other groups of
+  //    the request (the same sum that its own pick over the tile sums computes).
+  double* tsum = s_buf;                // [kChunkTiles]
   double* ctot = s_buf + kChunkTiles;  // [kMaxC2]
   const int t0 = (int)((long)NT * c2 / C2), t1 = (int)((long)NT * (c2 + 1) / C2);
   if (resid) tile_sums<T, VEC, true>(rt, rd, w, c32, G, t0, t1, tsum);
   else tile_sums<T, VEC, false>(rt, rd, w, c32, G, t0, t1, tsum);
   __syncthreads();
-  const double mine = lds_pick(tsum, t1 - t0, -1.0, INFINITY, red, ired).total;
   uint64_t* ct = a.ctot + (size_t)b * C2 * 2;
-  if (threadIdx.x == 0) {
-    const uint64_t bits = (uint64_t)__double_as_longlong(mine);
-    publish(&ct[2 * c2], tag, (uint32_t)(bits >> 32));
-    publish(&ct[2 * c2 + 1], tag, (uint32_t)bits);
+  if (wave == 0) {
+    const double mine = wave_pick(tsum, t1 - t0, -1.0, INFINITY).total;
+    if (lane == 0) {
+      const uint64_t bits = (uint64_t)__double_as_longlong(mine);
+      publish(&ct[2 * c2], tag, (uint32_t)(bits >> 32));
+      publish(&ct[2 * c2 + 1], tag, (uint32_t)bits);
+    }
   }
 
-  // 6. Every chunk total of the request (awaited as above), then the chunk holding r * Z (same
-  //    answer in every group of the request).
+  // 6. Every chunk total of the request (awaited as above), then the chunk holding r * Z, in
+  //    every wave (the same answer in every wave and every group of the request).
   {
     bool late2 = false;
     for (int c0 = 0; c0 < C2; c0 += kBlock * 4) {
       const uint64_t* p[4];
+      bool live[4];
       uint64_t hi[4], lo[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         int c = c0 + u * kBlock + (int)threadIdx.x;
-        c = c < C2 ? c : C2 - 1;
+        live[u] = c < C2;
+        c = live[u] ? c : C2 - 1;
         p[u] = &ct[2 * c];
       }
-      late2 = late2 || !await4(p, tag, hi, lo);
+      late2 = late2 || !await4(p, live, tag, hi, lo);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int c = c0 + u * kBlock + (int)threadIdx.x;
@@ -979,29 +1035,24 @@ __device__ void draw_group(const SampleArgs& a, long j) {
       return;
     }
   }
-  const double r = (double)a.residual[b];
-  const Pick pc = lds_pick(ctot, C2, r, 0.0, red, ired);
+  const Pick pc = wave_pick(ctot, C2, r, 0.0);
   if (pc.idx < 0) {  // zero residual mass (rounding only): chunk 0's group draws from p_n
     if (c2 != 0) return;
-    const int y = full_row_draw<T, VEC>(rt, w, c32, G, NT, r, tsum, red, ired);
+    const int y = full_row_draw<T, VEC>(rt, w, c32, G, NT, r, tsum);
     if (threadIdx.x == 0) a.committed[(size_t)b * (K + 1) + n] = y < 0 ? 0 : y;
     return;
   }
-  if (pc.idx != c2) return;
+  if (pc.idx != c2 || wave != 0) return;
 
-  // 7. This group holds r * Z: the tile inside the chunk, then the token inside the tile.
-  Pick pt = lds_pick(tsum, t1 - t0, -1.0, pc.rel, red, ired);
-  if (threadIdx.x < 64) {
-    int y = -1;
-    if (pt.idx >= 0) {
-      const double rel = pc.found ? pt.rel : INFINITY;
-      y = resid ? tile_find<T, VEC, true>(rt, rd, w, c32, G, t0 + pt.idx, rel)
-                : tile_find<T, VEC, false>(rt, rd, w, c32, G, t0 + pt.idx, rel);
-    }
-    if (threadIdx.x == 0) s_y = y;
+  // 7. This group holds r * Z: wave 0 picks the tile inside the chunk, then the token inside it.
+  const Pick pt = wave_pick(tsum, t1 - t0, -1.0, pc.rel);
+  int y = -1;
+  if (pt.idx >= 0) {
+    const double rel = pc.found ? pt.rel : INFINITY;
+    y = resid ? tile_find<T, VEC, true>(rt, rd, w, c32, G, t0 + pt.idx, rel)
+              : tile_find<T, VEC, false>(rt, rd, w, c32, G, t0 + pt.idx, rel);
   }
-  __syncthreads();
-  if (threadIdx.x == 0) a.committed[(size_t)b * (K + 1) + n] = s_y < 0 ? 0 : s_y;
+  if (lane == 0) a.committed[(size_t)b * (K + 1) + n] = y < 0 ? 0 : y;
 }
 
 // Grid order: every row-stat group, then every draw group, so a draw group waits only on groups
@@ -1023,6 +1074,17 @@ __device__ __forceinline__ void merge_argmax(float& v, int& i, float v2, int i2)
     v = v2;
     i = i2;
   }
+}
+
+// (value, index) of the whole wave merged, wave-uniform.
+__device__ __forceinline__ void wave_merge_argmax(float& v, int& i) {
+#define SV_ARGMAX_STEP(CTRL, ROWS)                          \
+  merge_argmax(v, i, dpp_f32<CTRL, ROWS>(v, -INFINITY), \
+               (int)dpp_u32<CTRL, ROWS>((uint32_t)i, (uint32_t)INT_MAX))
+  SV_SCAN_STEPS(SV_ARGMAX_STEP);
+#undef SV_ARGMAX_STEP
+  v = lane_f32(v, 63);
+  i = (int)lane_u32((uint32_t)i, 63);
 }
 
 struct GreedyArgs {
@@ -1058,12 +1120,7 @@ __device__ void argmax_group(const GreedyArgs& a, long wg) {
   stream_groups<T, VEC, kUnroll, false>(row, row, g0, g1, acc);
   float best = acc.best;
   int bi = acc.idx;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const float v2 = __shfl_xor(best, m);
-    const int i2 = __shfl_xor(bi, m);
-    merge_argmax(best, bi, v2, i2);
-  }
+  wave_merge_argmax(best, bi);
   __shared__ float sv[kWaves];
   __shared__ int si[kWaves];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1093,14 +1150,16 @@ __device__ void finish_group(const GreedyArgs& a, int b) {
   bool late = false;
   for (int e0 = 0; e0 < nent; e0 += kBlock * 4) {
     const uint64_t* p[4];
+    bool live[4];
     uint64_t wv[4], wi[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       int e = e0 + u * kBlock + (int)threadIdx.x;
-      e = e < nent ? e : nent - 1;
+      live[u] = e < nent;
+      e = live[u] ? e : nent - 1;
       p[u] = a.gstats + ((size_t)b * NR * C + e) * 2;  // rows 0..k come first
     }
-    late = late || !await4(p, tag, wv, wi);
+    late = late || !await4(p, live, tag, wv, wi);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int e = e0 + u * kBlock + (int)threadIdx.x;
