@@ -63,6 +63,7 @@ constexpr int kStageMax = 2048;   // partials of one request staged in LDS: (2K+
 constexpr int kChunkTiles = 512;  // draw tiles per draw group, at most
 constexpr int kMaxC2 = 512;       // draw groups per request, at most
 constexpr int kDrawGroups = 1024;  // draw groups per launch the plan aims at
+constexpr int kLaneRowChunks = 32;  // up to this many chunks per row, one lane combines a row
 constexpr int kSpinLimit = 1 << 21;  // polls (about 1 us each) before a waiting group gives up
 constexpr int32_t kTimedOut = -2;    // accepted_len value reported by a group that gave up
 constexpr int kPollSleep = 2;        // s_sleep units (64 clocks each) between two polls
@@ -489,7 +490,6 @@ struct SampleArgs {
   const float* residual;
   float c32;  // log2(e) / temperature, rounded to fp32
   int C, C2, NT;
-  long n_stat_groups;  // B * (2K+1) * C: groups before this index are row-stat groups
   uint32_t tag;        // this call's tag
   uint64_t* stats;
   uint64_t* gath;  // [B][K][2]
@@ -632,20 +632,22 @@ struct TileRows {
 // Staged row-stat entry that merges as nothing: offset -FLT_MAX, sum 0.
 constexpr uint64_t kEmptyStat = (uint64_t)0xff7fffffu << 32;
 
-// Merge of a chunk partial (o2, s2) into a row normaliser (O, S) in fp64. Offsets are integers,
-// so rescaling by 2^(o - O) is exact and the result does not depend on the order in which
-// larger offsets arrive (up to the order of the additions).
-__device__ __forceinline__ void merge_stats_f64(float& O, double& S, float o2, double s2) {
-  if (o2 > O) {
-    float d = O - o2;
-    d = d < -2000.0f ? -2000.0f : d;
-    S = ldexp(S, (int)d) + s2;
-    O = o2;
-  } else {
-    float d = o2 - O;
-    d = d < -2000.0f ? -2000.0f : d;
-    S += ldexp(s2, (int)d);
+// Merges eight staged partials v[0..7] into (O, S): the new offset is the largest of them all,
+// then every term is rescaled to it (exact) and added in order. Branch-free; equal, up to the
+// order of the additions, to merging them one at a time.
+__device__ __forceinline__ void merge_stats8(float& O, double& S, const uint64_t (&v)[8]) {
+  float on = O;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) on = fmaxf(on, __uint_as_float((uint32_t)(v[u] >> 32)));
+  float d = fmaxf(O - on, -2000.0f);
+  double acc = ldexp(S, (int)d);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    d = fmaxf(__uint_as_float((uint32_t)(v[u] >> 32)) - on, -2000.0f);
+    acc += ldexp((double)__uint_as_float((uint32_t)v[u]), (int)d);
   }
+  O = on;
+  S = acc;
 }
 
 // Merges the (O, S) pairs of aligned groups of RL lanes (RL a power of two, at most 64); every
@@ -843,6 +845,31 @@ __device__ int full_row_draw(const T* rt, const DrawParams& w, float c32, int G,
   return y;
 }
 
+// True in every thread of the group when v is true in any thread: one barrier. `flags` is a
+// kWaves-entry LDS array that no other code touches between the barrier before and after.
+__device__ __forceinline__ bool block_any(bool v, int* flags) {
+  const uint64_t m = __ballot(v);
+  if ((threadIdx.x & 63) == 0) flags[threadIdx.x >> 6] = m != 0;
+  __syncthreads();
+  bool any = false;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) any = any || flags[w] != 0;
+  return any;
+}
+
+// Normaliser (O, S) of one row from its C staged partials, by one lane, eight LDS reads in
+// flight at a time.
+__device__ __forceinline__ void row_norm(const uint64_t* st, int C, float& O, double& S) {
+  O = -FLT_MAX;
+  S = 0.0;
+  for (int c0 = 0; c0 < C; c0 += 8) {
+    uint64_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = c0 + u < C ? st[c0 + u] : kEmptyStat;
+    merge_stats8(O, S, v);
+  }
+}
+
 // Draw group j = b * C2 + c2; chunk c2 covers tiles [NT*c2/C2, NT*(c2+1)/C2).
 template <typename T, bool VEC>
 __device__ void draw_group(const SampleArgs& a, long j) {
@@ -855,11 +882,13 @@ __device__ void draw_group(const SampleArgs& a, long j) {
   const uint32_t tag = a.tag;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
-  // s_buf first stages the row-stat partials, then holds tile sums and chunk totals.
+  // s_buf stages the row-stat partials from its start, and holds tile sums and chunk totals at
+  // its end.
   __shared__ double s_buf[kStageMax];
   __shared__ float s_o[2 * kMaxK + 1];
   __shared__ double s_S[2 * kMaxK + 1];
   __shared__ float s_zt[kMaxK], s_zd[kMaxK];
+  __shared__ int s_late1[kWaves], s_late2[kWaves];
   uint64_t* stage = reinterpret_cast<uint64_t*>(s_buf);
 
   // Per-request inputs, read before the wait. Lane i < k of every wave holds slot i.
@@ -904,15 +933,22 @@ __device__ void draw_group(const SampleArgs& a, long j) {
       }
     }
   }
-  if (__syncthreads_or(late)) {
+  if (block_any(late, s_late1)) {
     if (threadIdx.x == 0) a.accepted_len[b] = kTimedOut;
     return;
   }
 
-  // 2. Row normalisers: the C partials of each used row combined in fp64. Row r is handled by
-  //    RL lanes (RL = 1 unless C > 16), lane li taking chunks li, li + RL, ... in order, eight
-  //    LDS reads in flight at a time; the RL lanes of a row then merge their (O, S) pairs.
-  {
+  // 2. Normalisers of the rows that slot `lane` uses, in every wave: target row lane
+  //    (lane <= k) and draft row lane (lane < k); with k = 64 lane 0 also takes target row 64.
+  //    Up to kLaneRowChunks chunks per row one lane combines a row; beyond that RL lanes share
+  //    a row and the results go through LDS.
+  float Ot = -FLT_MAX, Od = -FLT_MAX, Ox = -FLT_MAX;
+  double St = 0.0, Sd = 0.0, Sx = 0.0;
+  if (C <= kLaneRowChunks) {
+    if (lane <= k) row_norm(stage + lane * C, C, Ot, St);
+    if (lane < k) row_norm(stage + (k + 1 + lane) * C, C, Od, Sd);
+    if (k == kMaxK && lane == 0) row_norm(stage + kMaxK * C, C, Ox, Sx);
+  } else {
     int RL = 1;
     while (RL * 16 < C) RL <<= 1;  // C <= kStageMax, so RL <= 128: capped below
     RL = RL > 64 ? 64 : RL;
@@ -930,32 +966,39 @@ __device__ void draw_group(const SampleArgs& a, long j) {
           const int c = c0 + u * RL;
           v[u] = c < C ? st[c] : kEmptyStat;
         }
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          merge_stats_f64(O, S, __uint_as_float((uint32_t)(v[u] >> 32)),
-                          (double)__uint_as_float((uint32_t)v[u]));
+        merge_stats8(O, S, v);
       }
-      if (RL > 1) merge_row_lanes(O, S, RL);
+      merge_row_lanes(O, S, RL);
       if (live && li == 0) {
         const int slot = row <= k ? row : K + 1 + (row - k - 1);
         s_o[slot] = O;
         s_S[slot] = S;
       }
     }
+    __syncthreads();
+    if (lane <= k) {
+      Ot = s_o[lane];
+      St = s_S[lane];
+    }
+    if (lane < k) {
+      Od = s_o[K + 1 + lane];
+      Sd = s_S[K + 1 + lane];
+    }
+    if (k == kMaxK && lane == 0) {
+      Ox = s_o[kMaxK];
+      Sx = s_S[kMaxK];
+    }
   }
-  __syncthreads();
 
-  // 3. p(x), q(x), the accept decisions and the first rejection n, in every wave (lane i holds
-  //    slot i), so that n is known to each wave without another barrier.
+  // 3. p(x), q(x), the accept decisions and the first rejection n, in every wave.
   int n;
   {
     double p = 0.0, q = 0.0;
     bool rej = false;
     if (lane < k) {
       if (want_x) {
-        p = exp2((double)s_zt[lane] * (double)c32 - (double)s_o[lane]) / s_S[lane];
-        q = exp2((double)s_zd[lane] * (double)c32 - (double)s_o[K + 1 + lane]) /
-            s_S[K + 1 + lane];
+        p = exp2((double)s_zt[lane] * (double)c32 - (double)Ot) / St;
+        q = exp2((double)s_zd[lane] * (double)c32 - (double)Od) / Sd;
       }
       const double t = q > 0.0 ? fmin(1.0, p / q) : (p > 0.0 ? 1.0 : 0.0);
       rej = !((double)uni < t);
@@ -973,10 +1016,10 @@ __device__ void draw_group(const SampleArgs& a, long j) {
   DrawParams w;
   w.n = n;
   w.resid = resid ? 1 : 0;
-  w.oT = s_o[n];
-  w.iT = (float)(1.0 / s_S[n]);
-  w.oD = resid ? s_o[K + 1 + n] : 0.0f;
-  w.iD = resid ? (float)(1.0 / s_S[K + 1 + n]) : 0.0f;
+  w.oT = n < 64 ? lane_f32(Ot, n) : lane_f32(Ox, 0);
+  w.iT = (float)(1.0 / (n < 64 ? lane_f64(St, n) : lane_f64(Sx, 0)));
+  w.oD = resid ? lane_f32(Od, n) : 0.0f;
+  w.iD = resid ? (float)(1.0 / lane_f64(Sd, n)) : 0.0f;
   if (c2 == 0) {
     for (int i = threadIdx.x; i <= K; i += kBlock) {
       if (i < n) a.committed[(size_t)b * (K + 1) + i] = a.tokens[(size_t)b * K + i];
@@ -989,9 +1032,12 @@ __device__ void draw_group(const SampleArgs& a, long j) {
   const int G = VEC ? V / E : V;
 
   // 5. Tile sums of this chunk (LDS); wave 0 publishes the chunk total for the other groups of
-  //    the request (the same sum that its own pick over the tile sums computes).
-  double* tsum = s_buf;                // [kChunkTiles]
-  double* ctot = s_buf + kChunkTiles;  // [kMaxC2]
+  //    the request (the same sum that its own pick over the tile sums computes). Tile sums and
+  //    chunk totals sit at the end of s_buf; when the staged partials reach that far, every
+  //    wave must be done reading them first.
+  double* tsum = s_buf + kStageMax - kChunkTiles - kMaxC2;  // [kChunkTiles]
+  double* ctot = tsum + kChunkTiles;                         // [kMaxC2]
+  if (nent > kStageMax - kChunkTiles - kMaxC2) __syncthreads();
   const int t0 = (int)((long)NT * c2 / C2), t1 = (int)((long)NT * (c2 + 1) / C2);
   if (resid) tile_sums<T, VEC, true>(rt, rd, w, c32, G, t0, t1, tsum);
   else tile_sums<T, VEC, false>(rt, rd, w, c32, G, t0, t1, tsum);
@@ -1030,7 +1076,7 @@ __device__ void draw_group(const SampleArgs& a, long j) {
               (long long)(((uint64_t)payload(hi[u]) << 32) | payload(lo[u])));
       }
     }
-    if (__syncthreads_or(late2)) {
+    if (block_any(late2, s_late2)) {
       if (threadIdx.x == 0) a.accepted_len[b] = kTimedOut;
       return;
     }
@@ -1056,13 +1102,14 @@ __device__ void draw_group(const SampleArgs& a, long j) {
 }
 
 // Grid order: every row-stat group, then every draw group, so a draw group waits only on groups
-// dispatched before it. (Interleaving each request's draw groups a few requests behind its
-// row-stat groups measured slower: a waiting draw group takes a work-group slot from the stream.)
+// dispatched before it (and on its siblings, next to it in the grid). Draw groups placed among
+// the row-stat groups measured slower: while one waits, it holds a slot the stream could use.
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kBlock) void sv_verify_sample(SampleArgs a) {
   const long wg = blockIdx.x;
-  if (wg < a.n_stat_groups) row_stat_group<T, VEC>(a, wg);
-  else draw_group<T, VEC>(a, wg - a.n_stat_groups);
+  const long n_stat = (long)a.B * (2 * a.K + 1) * a.C;
+  if (wg < n_stat) row_stat_group<T, VEC>(a, wg);
+  else draw_group<T, VEC>(a, wg - n_stat);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1166,7 +1213,8 @@ __device__ void finish_group(const GreedyArgs& a, int b) {
       if (e < nent) stage[e] = ((uint64_t)payload(wv[u]) << 32) | payload(wi[u]);
     }
   }
-  if (__syncthreads_or(late)) {
+  __shared__ int s_late[kWaves];
+  if (block_any(late, s_late)) {
     if (threadIdx.x == 0) a.accepted_len[b] = kTimedOut;
     return;
   }
@@ -1347,7 +1395,6 @@ int sv_verify_batch(const void* target_logits, const void* draft_logits, int dty
   a.C = p.C;
   a.C2 = p.C2;
   a.NT = p.NT;
-  a.n_stat_groups = n_stat;
   a.tag = next_tag();
   a.stats = reinterpret_cast<uint64_t*>(ws + L.stats);
   a.gath = reinterpret_cast<uint64_t*>(ws + L.gath);
