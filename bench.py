@@ -6,8 +6,10 @@ A step is one sv_verify_batch (or sv_verify_greedy) call over one batch of synth
 is already resident in HBM. Several copies of the inputs at distinct addresses are rotated so that
 no step finds its rows in the 256 MB Infinity Cache from the previous step. Prints one JSON line:
 verified draft positions per second (the sum over requests of the drafts verified), with the
-achieved HBM bandwidth of the verify call against the MI355X peak, and the fp64 CPU oracle
-timed on a bounded sample of the same workload on this host.
+achieved HBM bandwidth of the verify call against the MI355X peak and against the read-stream
+ceiling this device reaches with a plain read probe over the same input copies, and the fp64
+CPU oracle timed on a bounded sample of the same workload on this host (one thread, and a pool
+of worker processes over requests).
 """
 import argparse
 import ctypes
@@ -36,6 +38,11 @@ def parse():
                     help="rotate input copies until at least this many bytes are cycled")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU budget of the oracle baseline (0 = skip)")
+    ap.add_argument("--cpu-workers", type=int, default=16,
+                    help="worker processes of the pooled oracle baseline (capped by the cores "
+                         "this process may use; 0 = skip the pooled baseline)")
+    ap.add_argument("--skip-ceiling", action="store_true",
+                    help="do not measure the read-stream ceiling")
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
     return ap.parse_args()
 
@@ -87,31 +94,119 @@ def measured_traffic(workload_name):
     return float(fields["traffic_bytes_per_call"]) if "traffic_bytes_per_call" in fields else None
 
 
-def cpu_baseline(inp, budget_s):
-    """The fp64 oracle, as it stands, on the first requests of the workload until the budget is
-    spent (at least one request). Single thread (numpy elementwise work)."""
+def _oracle_request(task):
+    """One request through the fp64 oracle (runs in the bench process or a pool worker)."""
     import oracle
 
+    mode, dtype, tau, K, k, target, draft, tokens, uniforms, residual = task
+    if mode == "sample":
+        oracle.verify_request(target, draft, dtype, tokens, uniforms, residual, tau, k, K)
+    else:
+        oracle.verify_greedy_request(target, dtype, tokens, k, K)
+    return k
+
+
+def _task(inp, b):
+    w = inp.workload
+    return (w.mode, w.dtype, w.temperature, w.K, inp.k_of(b), inp.target[b],
+            None if inp.draft is None else inp.draft[b], inp.tokens[b],
+            None if inp.uniforms is None else inp.uniforms[b],
+            None if inp.residual is None else float(inp.residual[b]))
+
+
+def cpu_baseline(inp, budget_s):
+    """The fp64 oracle, as it stands, on the first requests of the workload until the budget is
+    spent (at least one request). One thread (its work is elementwise numpy)."""
     w = inp.workload
     t0 = time.perf_counter()
     done, positions = 0, 0
     while done < w.B:
-        b = done
-        k = inp.k_of(b)
-        if w.mode == "sample":
-            oracle.verify_request(inp.target[b], inp.draft[b], w.dtype, inp.tokens[b],
-                                  inp.uniforms[b], float(inp.residual[b]), w.temperature, k,
-                                  w.K)
-        else:
-            oracle.verify_greedy_request(inp.target[b], w.dtype, inp.tokens[b], k, w.K)
+        positions += _oracle_request(_task(inp, done))
         done += 1
-        positions += k
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
     return {"value": positions / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
             "sample": f"first {done} of {w.B} requests of {w.name} ({positions} positions, "
                       f"{dt:.1f} s, fp64 numpy, one thread)"}
+
+
+def cpu_baseline_pool(inp, budget_s, workers):
+    """The same oracle over requests in a pool of worker processes (spawned, so they hold no GPU
+    state; each imports numpy and the oracle only). Requests are handed out until about
+    budget_s of wall time has gone; the rate counts the requests finished by then."""
+    import multiprocessing as mp
+
+    w = inp.workload
+    cores = min(workers, len(os.sched_getaffinity(0)))
+    if cores < 1:
+        return None
+    ctx = mp.get_context("spawn")
+    saved = os.environ.get("OMP_NUM_THREADS")
+    os.environ["OMP_NUM_THREADS"] = "1"  # inherited by the workers: one thread each
+    try:
+        pool = ctx.Pool(cores)
+    finally:
+        if saved is None:
+            del os.environ["OMP_NUM_THREADS"]
+        else:
+            os.environ["OMP_NUM_THREADS"] = saved
+    with pool:
+        pool.map(_oracle_request, [_task(inp, 0)] * cores)  # start-up and imports, untimed
+        t0 = time.perf_counter()
+        done, positions = 0, 0
+        pending = []
+        b = 0
+        while b < w.B or pending:
+            while b < w.B and len(pending) < 2 * cores and time.perf_counter() - t0 < budget_s:
+                pending.append(pool.apply_async(_oracle_request, (_task(inp, b),)))
+                b += 1
+            if not pending:
+                break
+            positions += pending.pop(0).get()
+            done += 1
+        dt = time.perf_counter() - t0
+    return {"value": positions / dt, "unit": "positions/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {w.B} requests of {w.name} ({positions} positions, {dt:.1f} s, "
+                      f"fp64 numpy, a pool of {cores} worker processes, one request per task)"}
+
+
+def read_ceiling(lib, call_bytes, dev, stream):
+    """Read bandwidth of this device with the library's read probe (every 16-byte word read once
+    with non-temporal loads, a plain sum per work-group), the best over a few grid sizes:
+    (1) one launch over a 2 GiB buffer, the streaming ceiling; (2) one launch per call-sized
+    slice, rotated over disjoint slices of that buffer, the ceiling for a launch of this size
+    (start-up and drain included). GB/s of bytes read."""
+    import torch
+
+    total = 2 << 30
+    buf = torch.empty(total, dtype=torch.uint8, device=dev)
+    size = max(16, min(call_bytes, total // 4) // 16 * 16)
+    slices = [i * size for i in range(total // size)]
+
+    def timed(args, reps):
+        for a in args:
+            if lib.sv_read_probe(*a) != 0:
+                raise RuntimeError("sv_read_probe failed")
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            for a in args:
+                lib.sv_read_probe(*a)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return sum(a[1] for a in args) * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+    big = same = 0.0
+    for groups in (1024, 2048, 4096, 8192):
+        out = torch.empty(groups, dtype=torch.int32, device=dev)
+        sp = stream.cuda_stream
+        big = max(big, timed([(buf.data_ptr(), total, out.data_ptr(), groups, sp)], 5))
+        same = max(same, timed([(buf.data_ptr() + o, size, out.data_ptr(), groups, sp)
+                                for o in slices], 5))
+    del buf
+    return big, same
 
 
 def main():
@@ -128,6 +223,9 @@ def main():
 
     w = pick_workload(args.workload)
     inp = generate(w)
+    # the pooled oracle runs first, before this process touches the GPU
+    pooled = (cpu_baseline_pool(inp, args.cpu_seconds, args.cpu_workers)
+              if args.cpu_seconds > 0 and args.cpu_workers > 0 else None)
     dev = torch.device("cuda:0")
 
     def up(a):
@@ -235,8 +333,16 @@ def main():
                      "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(w.name)},
     }
+    if not args.skip_ceiling:
+        big, same = read_ceiling(lib, alg_bytes, dev, stream)
+        result["read_ceiling_gbps"] = big
+        result["frac_of_read_ceiling"] = gbps / big
+        result["read_probe_call_size_gbps"] = same
+        result["frac_of_call_size_probe"] = gbps / same
     if args.cpu_seconds > 0:
-        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        single = cpu_baseline(inp, args.cpu_seconds)
+        result["cpu_baseline"] = pooled if pooled is not None else single
+        result["cpu_baseline_one_thread"] = single
     line = json.dumps(result)
     print(line, flush=True)
     if args.out:

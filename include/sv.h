@@ -115,6 +115,20 @@ int sv_verify_greedy(const void* target_logits, int dtype, int B, int K, int V,
                      int32_t* accepted_len, int32_t* committed, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/* Read probe (a measurement aid, not a step of the method): the plainest stream over a device
+ * buffer, so that the row stream can be compared with the read bandwidth this device reaches.
+ * `groups` work-groups of 256 threads read every 16-byte word of data[0, bytes) once with
+ * non-temporal loads, group g a contiguous 1/groups of the words; group g writes the wrapping
+ * 32-bit sum of its words to partial[g].
+ *
+ *  data     device pointer, 16-byte aligned; bytes a multiple of 16 (0 is allowed)
+ *  partial  device pointer, [groups] uint32 out, owned by the caller
+ *  groups   1 .. 2^20
+ *  stream   hipStream_t (NULL = default stream); the call is asynchronous
+ * Returns SV_OK, SV_ERR_INVALID_ARG (nothing launched) or SV_ERR_HIP.
+ */
+int sv_read_probe(const void* data, size_t bytes, uint32_t* partial, int groups, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -58,6 +58,8 @@ def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
         lib.sv_verify_batch.restype = i32
         lib.sv_verify_greedy.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
         lib.sv_verify_greedy.restype = i32
+        lib.sv_read_probe.argtypes = [vp, sz, vp, i32, vp]
+        lib.sv_read_probe.restype = i32
         _lib = lib
         return lib
 
@@ -187,3 +189,17 @@ def sv_verify_greedy(target: torch.Tensor, draft_tokens: torch.Tensor,
         _ptr(target), _dtype_code(target), B, K, V, _ptr(draft_tokens), _ptr(num_draft),
         _ptr(acc), _ptr(com), _ptr(ws), ws.numel(), stream))
     return VerifyOutput(acc, com, None, None)
+
+
+def sv_read_probe(data: torch.Tensor, groups: int = 2048) -> torch.Tensor:
+    """Read probe over a contiguous GPU tensor (see sv_read_probe in include/sv.h): every
+    16-byte word read once with non-temporal loads. Returns the [groups] uint32 partial sums
+    (as int32). Asynchronous on the current stream."""
+    lib = load_library()
+    if data.device.type != "cuda" or not data.is_contiguous():
+        raise ValueError("data must be a contiguous GPU tensor")
+    nbytes = data.numel() * data.element_size()
+    out = torch.empty(groups, dtype=torch.int32, device=data.device)
+    stream = torch.cuda.current_stream(data.device).cuda_stream
+    _check(lib.sv_read_probe(_ptr(data), nbytes - nbytes % 16, _ptr(out), groups, stream))
+    return out

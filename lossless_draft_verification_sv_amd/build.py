@@ -11,7 +11,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "sv_kernels.hip")
+SRCS = [os.path.join(PKG, "csrc", "sv_kernels.hip"), os.path.join(PKG, "csrc", "sv_probe.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsv.so")
 
@@ -35,7 +35,7 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     """Compile libsv.so (always recompiles). Returns its path."""
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-o", tmp, SRC]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-o", tmp, *SRCS]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -48,6 +48,7 @@
 #include <string>
 
 #include "sv.h"
+#include "sv_internal.h"
 
 namespace {
 
@@ -1330,6 +1331,10 @@ int launch_greedy(const GreedyArgs& a, long groups, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Error reporting shared with the library's other source files (sv_internal.h).
+int sv_internal_fail(int status, const char* msg) { return fail(status, msg); }
+void sv_internal_clear_error() { g_last_error.clear(); }
 
 extern "C" {
 

@@ -138,3 +138,20 @@ def test_python_binding_rejects_bad_tensors():
     with pytest.raises((TypeError, ValueError)):
         sv.sv_verify_greedy(torch.zeros(2, 5, 10, dtype=torch.float64),
                             torch.zeros(2, 4, dtype=torch.int32))
+
+
+def test_read_probe_rejects_invalid_arguments(lib):
+    buf = (ctypes.c_uint8 * 64)()
+    base = ctypes.addressof(buf)
+    aligned = base + (-base) % 16
+    out = (ctypes.c_uint32 * 4)()
+    probe = ctypes.CDLL(sv.LIBRARY_PATH).sv_read_probe
+    probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                      ctypes.c_void_p]
+    probe.restype = ctypes.c_int
+    assert probe(None, 16, ctypes.addressof(out), 4, None) == sv.SV_ERR_INVALID_ARG
+    assert probe(aligned, 16, None, 4, None) == sv.SV_ERR_INVALID_ARG
+    assert probe(aligned + 4, 16, ctypes.addressof(out), 4, None) == sv.SV_ERR_INVALID_ARG
+    assert probe(aligned, 12, ctypes.addressof(out), 4, None) == sv.SV_ERR_INVALID_ARG
+    assert probe(aligned, 16, ctypes.addressof(out), 0, None) == sv.SV_ERR_INVALID_ARG
+    assert "16-byte" in sv.sv_last_error() or "groups" in sv.sv_last_error()
