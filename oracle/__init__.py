@@ -3,13 +3,14 @@
 Imported by the tests, the smoke check and the benchmark's CPU-baseline leg; never by the GPU
 library.
 """
-from .sv_oracle import (AMBIGUOUS_MARGIN, BatchResult, RequestResult, accept_threshold,
-                        argmax_lowest, decode_logits, inverse_cdf, residual_weights,
-                        softmax_fp64, verify_batch, verify_greedy, verify_greedy_request,
-                        verify_request)
+from .sv_oracle import (AMBIGUOUS_MARGIN, RAGGED_INVALID, TAU_MIN, BatchResult, RequestResult,
+                        accept_threshold, argmax_lowest, decode_logits, inverse_cdf,
+                        ragged_request_valid, residual_weights, softmax_fp64, verify_batch,
+                        verify_greedy, verify_greedy_request, verify_ragged, verify_request)
 
 __all__ = [
-    "AMBIGUOUS_MARGIN", "BatchResult", "RequestResult", "accept_threshold", "argmax_lowest",
-    "decode_logits", "inverse_cdf", "residual_weights", "softmax_fp64", "verify_batch",
-    "verify_greedy", "verify_greedy_request", "verify_request",
+    "AMBIGUOUS_MARGIN", "RAGGED_INVALID", "TAU_MIN", "BatchResult", "RequestResult",
+    "accept_threshold", "argmax_lowest", "decode_logits", "inverse_cdf", "ragged_request_valid",
+    "residual_weights", "softmax_fp64", "verify_batch", "verify_greedy", "verify_greedy_request",
+    "verify_ragged", "verify_request",
 ]

@@ -33,6 +33,11 @@ Readings taken where the pages leave a step open:
   * per-request draft counts k_b in [0, K]: only slots < k_b are verified, the bonus comes from
     target row k_b, rows past k_b are never read, masked outputs are -1 / 0;
   * greedy argmax ties go to the lowest vocabulary index, compared on the stored values;
+  * a flattened batch packs each request's used rows (k_b+1 target, k_b draft) at a start index
+    of its own; a request with temperature 0 in a mixed batch is a greedy request and any other
+    request samples at its own temperature; a request whose rows fall outside the flat arrays,
+    whose k_b is outside [0, K] or whose temperature is negative, not finite or below TAU_MIN is
+    reported invalid (RAGGED_INVALID) without reading anything;
   * bf16 logits are decoded exactly from their bit patterns; all arithmetic is fp64.
 
 The parity harness also needs to know which requests are too close to a decision threshold for
@@ -223,7 +228,7 @@ class BatchResult:
 
     @property
     def ambiguous(self) -> np.ndarray:
-        return np.array([r.ambiguous for r in self.requests], dtype=bool)
+        return np.array([r is not None and r.ambiguous for r in self.requests], dtype=bool)
 
 
 def _k_of(num_draft, b: int, K: int) -> int:
@@ -268,3 +273,75 @@ def verify_greedy(target: np.ndarray, dtype: str, tokens: np.ndarray,
         n, c = verify_greedy_request(target[b], dtype, tokens[b], k, K)
         acc[b], com[b] = n, c
     return BatchResult(acc, com, np.zeros((B, K)), None, [None] * B)
+
+
+# ---------------------------------------------------------------------------------------------
+# Flattened, mixed batches: the per-request verify lengths of one batch packed without padding,
+# each request's rows found through its start index ("flatten every token and track its request
+# ID", the DSpark paper review, 4.2.2), and greedy and sampling requests in one batch (the vLLM
+# Metal article's greedy-only path, with sampled verification listed as still in flight).
+
+RAGGED_INVALID = -3  # accepted_len of a request whose rows, k_b or temperature are invalid
+# Smallest positive temperature a sampling request may have: the scale log2(e) / tau of the
+# logits must not exceed 2^21.
+TAU_MIN = 1.4426950408889634 / 2.0 ** 21
+
+
+def ragged_request_valid(k: int, K: int, tau: float, ts: int, ds: int, n_target_rows: int,
+                         n_draft_rows: int) -> bool:
+    """A request of a flattened batch is valid when 0 <= k <= K, its temperature is 0 (greedy)
+    or in [TAU_MIN, inf), its k+1 target rows lie inside the flat target array and, when it
+    samples and k > 0, its k draft rows lie inside the flat draft array."""
+    if not 0 <= k <= K:
+        return False
+    if not (tau == 0.0 or (TAU_MIN <= tau < float("inf"))):
+        return False
+    if ts < 0 or ts + k + 1 > n_target_rows:
+        return False
+    if tau != 0.0 and k > 0 and (ds < 0 or ds + k > n_draft_rows):
+        return False
+    return True
+
+
+def verify_ragged(target_flat: np.ndarray, draft_flat: Optional[np.ndarray], dtype: str,
+                  tokens: np.ndarray, uniforms: np.ndarray, residual: np.ndarray,
+                  temperatures: np.ndarray, num_draft: np.ndarray, target_row_start: np.ndarray,
+                  draft_row_start: np.ndarray, requests: Optional[list] = None) -> BatchResult:
+    """Verification of a flattened, mixed batch.
+
+    target_flat [rows_t, V] and draft_flat [rows_d, V] hold the stored logit rows of all
+    requests; request b's target rows are target_flat[target_row_start[b] + i] for i = 0..k_b and
+    its draft rows draft_flat[draft_row_start[b] + i] for i < k_b. tokens and uniforms are
+    [B, K] (entries past k_b unused), residual [B]. temperatures[b] == 0 makes request b a
+    greedy request (its draft rows, uniforms and residual are not used; its probabilities are
+    reported as 0); otherwise it is a sampling request at temperature temperatures[b]. Each
+    request is then exactly verify_greedy_request or verify_request on its own rows. An invalid
+    request (see ragged_request_valid) gets accepted_len RAGGED_INVALID, committed all -1 and
+    probabilities 0, and none of its rows is read.
+    """
+    B, K = tokens.shape
+    rows_t = target_flat.shape[0]
+    rows_d = 0 if draft_flat is None else draft_flat.shape[0]
+    idx = range(B) if requests is None else requests
+    acc = np.full(B, -1, dtype=np.int32)
+    com = np.full((B, K + 1), -1, dtype=np.int32)
+    tp = np.zeros((B, K))
+    dp = np.zeros((B, K))
+    res = [None] * B
+    for b in idx:
+        k = int(num_draft[b])
+        tau = float(temperatures[b])
+        ts, ds = int(target_row_start[b]), int(draft_row_start[b])
+        if not ragged_request_valid(k, K, tau, ts, ds, rows_t, rows_d):
+            acc[b] = RAGGED_INVALID
+            continue
+        t_rows = target_flat[ts:ts + k + 1]
+        if tau == 0.0:
+            acc[b], com[b] = verify_greedy_request(t_rows, dtype, tokens[b], k, K)
+            continue
+        d_rows = draft_flat[ds:ds + k] if k > 0 else target_flat[ts:ts]
+        rr = verify_request(t_rows, d_rows, dtype, tokens[b], uniforms[b], float(residual[b]),
+                            tau, k, K)
+        acc[b], com[b], tp[b], dp[b], res[b] = rr.n, rr.committed, rr.target_prob, \
+            rr.draft_prob, rr
+    return BatchResult(acc, com, tp, dp, res)

@@ -38,6 +38,16 @@ MUTATIONS = {
     "greedy_commits_previous_argmax": (
         "committed = [int(tokens[i]) for i in range(n)] + [g[n]] + [-1] * (K - n)",
         "committed = [int(tokens[i]) for i in range(n)] + [g[max(n - 1, 0)]] + [-1] * (K - n)"),
+    "ragged_target_start_off_by_one": (
+        "t_rows = target_flat[ts:ts + k + 1]", "t_rows = target_flat[ts + 1:ts + k + 2]"),
+    "ragged_draft_rows_from_target_start": (
+        "d_rows = draft_flat[ds:ds + k] if k > 0", "d_rows = draft_flat[ts:ts + k] if k > 0"),
+    "ragged_greedy_flag_inverted": ("        if tau == 0.0:\n            acc[b], com[b]",
+                                    "        if tau != 0.0:\n            acc[b], com[b]"),
+    "ragged_temperature_of_request_0": ("tau = float(temperatures[b])",
+                                        "tau = float(temperatures[0])"),
+    "ragged_draft_bound_unchecked": ("if tau != 0.0 and k > 0 and (ds < 0 or ds + k > n_draft_rows):",
+                                     "if tau != 0.0 and k > 0 and ds < 0:"),
     "greedy_ties_to_highest_index": (
         "best = int(np.argmax(values))",
         "best = int(len(values) - 1 - np.argmax(np.asarray(values)[::-1]))"),
@@ -47,6 +57,7 @@ CHECKS = [
     pins.check_decode, pins.check_softmax, pins.check_accept_threshold,
     pins.check_identical_rows_accept_all, pins.check_golden, pins.check_masking_and_edges,
     pins.check_inverse_cdf, pins.check_greedy_argmax, pins.check_greedy_decode_equals_target_only,
+    pins.check_ragged_golden, pins.check_ragged_invalid_requests,
     lambda: pins.check_single_slot_lossless(Vs=(3, 5), seeds=range(3)),
     lambda: pins.check_multi_slot_law(cases=((3, 2), (3, 3))),
 ]

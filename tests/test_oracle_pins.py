@@ -349,6 +349,95 @@ def check_golden():
             assert n == exp["accepted_len"] and com == exp["committed"], f
 
 
+def golden_flat_batch():
+    """Every golden worked example as one request of a single flattened, mixed batch.
+
+    Vocabularies are padded to the largest V with -inf logits (probability 0: no probability,
+    argmax or draw changes), K to the largest K (num_draft keeps each request's own k), requests
+    are packed in reverse file order with a NaN row between them, and each request keeps its own
+    temperature (0 for the greedy example). Returns the batch and the expected outputs."""
+    gs = [json.load(open(f)) for f in sorted(glob.glob(os.path.join(GOLDEN, "*.json")))]
+    V = max(g["V"] for g in gs)
+    K = max(g["K"] for g in gs)
+    B = len(gs)
+
+    def pad(rows):
+        rows = np.asarray(rows, dtype=np.float32)
+        out = np.full((rows.shape[0], V), -np.inf, dtype=np.float32)
+        out[:, :rows.shape[1]] = rows
+        return out
+
+    t_rows, d_rows = [], []
+    ts, ds = np.zeros(B, np.int32), np.zeros(B, np.int32)
+    tokens = np.full((B, K), -1, np.int32)
+    uni = np.full((B, K), np.nan)
+    res = np.zeros(B)
+    taus = np.zeros(B)
+    nd = np.zeros(B, np.int32)
+    expected = []
+    gap = np.full((1, V), np.nan, dtype=np.float32)
+    for b in reversed(range(B)):
+        g = gs[b]
+        k = g["K"] if g["num_draft"] is None else g["num_draft"]
+        nd[b] = k
+        tokens[b, :len(g["tokens"])] = g["tokens"]
+        if g["mode"] == "sample":
+            T = pad(logits_from_probs(g["target_probs"]))
+            D = pad(logits_from_probs(g["draft_probs"]))
+            uni[b, :len(g["uniforms"])] = g["uniforms"]
+            res[b] = g["residual"]
+            taus[b] = g["tau"]
+            ds[b] = sum(len(r) for r in d_rows)
+            d_rows += [D[:k], gap]
+        else:
+            T = pad(g["target_logits"])
+        ts[b] = sum(len(r) for r in t_rows)
+        t_rows += [T[:k + 1], gap]
+    for b, g in enumerate(gs):
+        e = g["expected"]
+        com = list(e["committed"]) + [-1] * (K + 1 - len(e["committed"]))
+        tp = list(e.get("target_prob", [])) + [0.0] * (K - len(e.get("target_prob", [])))
+        dp = list(e.get("draft_prob", [])) + [0.0] * (K - len(e.get("draft_prob", [])))
+        expected.append((e["accepted_len"], com, tp, dp))
+    batch = dict(target_flat=np.concatenate(t_rows), draft_flat=np.concatenate(d_rows),
+                 dtype="f32", tokens=tokens, uniforms=uni, residual=res, temperatures=taus,
+                 num_draft=nd, target_row_start=ts, draft_row_start=ds)
+    return batch, expected
+
+
+def check_ragged_golden():
+    batch, expected = golden_flat_batch()
+    out = O.verify_ragged(**batch)
+    for b, (n, com, tp, dp) in enumerate(expected):
+        assert out.accepted_len[b] == n, b
+        assert out.committed[b].tolist() == com, b
+        assert np.allclose(out.target_prob[b], tp, atol=1e-6), b
+        assert np.allclose(out.draft_prob[b], dp, atol=1e-6), b
+
+
+def check_ragged_invalid_requests():
+    batch, expected = golden_flat_batch()
+    rows_t = batch["target_flat"].shape[0]
+    B = len(expected)
+    cases = [("target_row_start", 0, -1), ("target_row_start", 0, rows_t - 1),
+             ("temperatures", 1, -0.5), ("temperatures", 1, np.nan),
+             ("temperatures", 1, np.inf), ("temperatures", 1, O.TAU_MIN / 2),
+             ("num_draft", 2, batch["tokens"].shape[1] + 1), ("num_draft", 2, -1)]
+    samp = [b for b in range(B) if batch["temperatures"][b] > 0][0]
+    cases.append(("draft_row_start", samp, batch["draft_flat"].shape[0]))
+    for key, b, val in cases:
+        bad = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in batch.items()}
+        bad[key][b] = val
+        out = O.verify_ragged(**bad)
+        assert out.accepted_len[b] == O.RAGGED_INVALID, (key, val)
+        assert out.committed[b].tolist() == [-1] * (bad["tokens"].shape[1] + 1)
+        assert not out.target_prob[b].any() and not out.draft_prob[b].any()
+        for o in range(B):  # the other requests are untouched
+            if o != b:
+                assert out.accepted_len[o] == expected[o][0], (key, o)
+                assert out.committed[o].tolist() == expected[o][1], (key, o)
+
+
 def check_masking_and_edges():
     rng = np.random.default_rng(6)
     K, V = 6, 50
@@ -451,3 +540,42 @@ def test_batch_driver_matches_per_request():
                                inp.uniforms[b], float(inp.residual[b]), w.temperature, w.K)
         assert res.committed[b].tolist() == one.committed
         assert res.accepted_len[b] == one.n
+
+
+def test_ragged_mixed_batch_reproduces_the_golden_examples():
+    check_ragged_golden()
+
+
+def test_ragged_invalid_requests_are_flagged_and_isolated():
+    check_ragged_invalid_requests()
+
+
+def test_ragged_driver_matches_padded_drivers():
+    """Flattening a padded batch (used rows only, packed in a shuffled order) changes nothing."""
+    from workloads import HEAVY, generate
+
+    inp = generate(HEAVY.replace(B=6, K=4, V=96, dtype="f32", seed=91))
+    w = inp.workload
+    B, K, V = w.B, w.K, w.V
+    order = [3, 0, 5, 1, 4, 2]
+    t_rows, d_rows, ts, ds = [], [], np.zeros(B, np.int32), np.zeros(B, np.int32)
+    for b in order:
+        k = inp.k_of(b)
+        ts[b] = sum(len(r) for r in t_rows)
+        ds[b] = sum(len(r) for r in d_rows)
+        t_rows.append(inp.target[b, :k + 1])
+        d_rows.append(inp.draft[b, :k])
+    tf, df = np.concatenate(t_rows), np.concatenate(d_rows)
+    taus = np.full(B, w.temperature)
+    out = O.verify_ragged(tf, df, w.dtype, inp.tokens, inp.uniforms, inp.residual, taus,
+                          inp.num_draft, ts, ds)
+    ref = O.verify_batch(inp.target, inp.draft, w.dtype, inp.tokens, inp.uniforms,
+                         inp.residual, w.temperature, inp.num_draft)
+    assert np.array_equal(out.accepted_len, ref.accepted_len)
+    assert np.array_equal(out.committed, ref.committed)
+    assert np.array_equal(out.target_prob, ref.target_prob)
+    out_g = O.verify_ragged(tf, df, w.dtype, inp.tokens, inp.uniforms, inp.residual,
+                            np.zeros(B), inp.num_draft, ts, ds)
+    ref_g = O.verify_greedy(inp.target, w.dtype, inp.tokens, inp.num_draft)
+    assert np.array_equal(out_g.accepted_len, ref_g.accepted_len)
+    assert np.array_equal(out_g.committed, ref_g.committed)
