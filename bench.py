@@ -33,7 +33,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="batched",
-                    help="tiny | interactive | batched | heavy | greedy | sweep_<mode>_<K>_<B>_<dtype>")
+                    help="tiny | interactive | batched | heavy | greedy | mixed | "
+                         "sweep_<mode>_<K>_<B>_<dtype>")
     ap.add_argument("--min-rotation-bytes", type=float, default=1.2e9,
                     help="rotate input copies until at least this many bytes are cycled")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -51,7 +52,7 @@ def pick_workload(name):
     import workloads as W
 
     named = {"tiny": W.TINY, "interactive": W.INTERACTIVE, "batched": W.BATCHED,
-             "heavy": W.HEAVY, "greedy": W.GREEDY}
+             "heavy": W.HEAVY, "greedy": W.GREEDY, "mixed": W.MIXED}
     if name in named:
         return named[name]
     if name.startswith("sweep_"):
@@ -66,12 +67,15 @@ def algorithmic_bytes(inp):
     w = inp.workload
     s = 2 if w.dtype == "bf16" else 4
     ks = np.array([inp.k_of(b) for b in range(w.B)], dtype=np.int64)
-    rows = (2 * ks + 1) if w.mode == "sample" else (ks + 1)
+    samples = np.array([w.temperature_of(b) > 0 for b in range(w.B)])
+    rows = np.where(samples, 2 * ks + 1, ks + 1)
     logits = int(rows.sum()) * w.V * s
     small = w.B * w.K * 4 + w.B * 4 * (1 if inp.num_draft is not None else 0)  # tokens, k_b
     small += w.B * (w.K + 1) * 4 + w.B * 4  # committed, accepted_len
-    if w.mode == "sample":
+    if w.mode != "greedy":
         small += w.B * w.K * 4 + w.B * 4 + w.B * w.K * 4  # uniforms, residual, target_prob
+    if w.mode == "mixed":
+        small += w.B * 4 * 3  # temperatures, row starts
     return logits + small, int(ks.sum())
 
 
@@ -99,7 +103,7 @@ def _oracle_request(task):
     import oracle
 
     mode, dtype, tau, K, k, target, draft, tokens, uniforms, residual = task
-    if mode == "sample":
+    if tau > 0:
         oracle.verify_request(target, draft, dtype, tokens, uniforms, residual, tau, k, K)
     else:
         oracle.verify_greedy_request(target, dtype, tokens, k, K)
@@ -108,7 +112,7 @@ def _oracle_request(task):
 
 def _task(inp, b):
     w = inp.workload
-    return (w.mode, w.dtype, w.temperature, w.K, inp.k_of(b), inp.target[b],
+    return (w.mode, w.dtype, w.temperature_of(b), w.K, inp.k_of(b), inp.target[b],
             None if inp.draft is None else inp.draft[b], inp.tokens[b],
             None if inp.uniforms is None else inp.uniforms[b],
             None if inp.residual is None else float(inp.residual[b]))
@@ -219,7 +223,7 @@ def main():
     import torch
 
     import lossless_draft_verification_sv_amd as sv
-    from workloads import generate
+    from workloads import flatten, generate
 
     w = pick_workload(args.workload)
     inp = generate(w)
@@ -236,15 +240,16 @@ def main():
                 torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    t0 = up(inp.target)
-    d0 = up(inp.draft)
+    flat = flatten(inp) if w.mode == "mixed" else None
+    t0 = up(inp.target if flat is None else flat.target)
+    d0 = up(inp.draft if flat is None else flat.draft)
     per_copy = t0.numel() * t0.element_size() + (0 if d0 is None else d0.numel() * d0.element_size())
     copies = max(1, int(np.ceil(args.min_rotation_bytes / per_copy)))
     targets = [t0] + [t0.clone() for _ in range(copies - 1)]
     drafts = [d0] + ([d0.clone() for _ in range(copies - 1)] if d0 is not None else
                      [None] * (copies - 1))
     tokens, uniforms, residual = up(inp.tokens), up(inp.uniforms), up(inp.residual)
-    num_draft = up(inp.num_draft)
+    num_draft = up(inp.num_draft if flat is None else flat.num_draft)
     B, K, V = w.B, w.K, w.V
     acc = torch.empty(B, dtype=torch.int32, device=dev)
     com = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
@@ -258,7 +263,14 @@ def main():
     P = lambda t: None if t is None else t.data_ptr()  # noqa: E731
 
     # Arguments of every step, built once: the timed loop only calls into the library.
-    if w.mode == "sample":
+    if w.mode == "mixed":
+        fn = lib.sv_verify_ragged
+        temps, ts, ds = up(flat.temperatures), up(flat.target_row_start), up(flat.draft_row_start)
+        rows_d = 0 if d0 is None else d0.shape[0]
+        argv = [(P(targets[c]), P(drafts[c]), code, B, K, V, t0.shape[0], rows_d, P(ts), P(ds),
+                 P(num_draft), P(temps), P(tokens), P(uniforms), P(residual), P(acc), P(com),
+                 P(tp), None, P(ws), nbytes, sptr) for c in range(copies)]
+    elif w.mode == "sample":
         fn = lib.sv_verify_batch
         argv = [(P(targets[c]), P(drafts[c]), code, B, K, V, float(w.temperature), P(tokens),
                  P(num_draft), P(uniforms), P(residual), P(acc), P(com), P(tp), None, P(ws),
@@ -329,7 +341,8 @@ def main():
         "algorithmic_bytes_per_call": alg_bytes,
         "mean_acceptance_length": float(np.mean(acc_np + 1)),
         "roofline": {"bound": "hbm",
-                     "kernel": "sv_verify_sample" if w.mode == "sample" else "sv_verify_greedy",
+                     "kernel": {"sample": "sv_verify_sample", "greedy": "sv_verify_greedy",
+                                "mixed": "sv_verify_ragged_kernel"}[w.mode],
                      "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": gbps / HBM_PEAK_GBPS, "traffic": measured_traffic(w.name)},
     }

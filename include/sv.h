@@ -115,6 +115,47 @@ int sv_verify_greedy(const void* target_logits, int dtype, int B, int K, int V,
                      int32_t* accepted_len, int32_t* committed, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/* Flattened, mixed-mode verification. The per-request verify lengths of one batch packed
+ * without padding, each request's rows found through its start index ("flatten every token and
+ * track its request ID", DSpark paper review 4.2.2), and greedy and sampling requests in one
+ * launch, each sampling request at its own temperature (the vLLM Metal article serves greedy
+ * requests only and lists sampled verification as in flight).
+ *
+ * Request b (0 <= b < B) verifies k_b = num_draft[b] drafts with
+ *   target rows  target_logits[target_row_start[b] + i], i = 0..k_b         (k_b + 1 rows)
+ *   draft rows   draft_logits[draft_row_start[b] + i],   i = 0..k_b - 1     (k_b rows)
+ * temperature[b] == 0: a greedy request, exactly as sv_verify_greedy on its target rows (its
+ *   draft rows, uniforms and residual uniform are not read; its probabilities are written 0);
+ * temperature[b] >= log2(e) / 2^21 and finite: a sampling request, exactly as sv_verify_batch
+ *   with that temperature on its rows.
+ * A request is invalid when k_b is outside [0, K], its temperature is negative, not finite or
+ * in (0, log2(e)/2^21), its target rows leave [0, n_target_rows), or (sampling, k_b > 0) its
+ * draft rows leave [0, n_draft_rows). Nothing of an invalid request is read; it reports
+ * accepted_len -3, committed all -1 and probabilities 0. The others are unaffected.
+ *
+ *  target_logits     [n_target_rows, V] dtype, device       draft_logits [n_draft_rows, V] dtype,
+ *                    (NULL allowed when n_draft_rows == 0)
+ *  target_row_start, draft_row_start, num_draft  [B] int32, device
+ *  temperature       [B] float, device
+ *  draft_tokens [B, K] int32, uniforms [B, K] float, residual_uniform [B] float (device; entries
+ *  past k_b unused); outputs as sv_verify_batch (accepted_len [B], committed [B, K+1],
+ *  target_prob [B, K], draft_prob [B, K] or NULL). K is the largest k_b the call allows.
+ *  workspace  sv_workspace_bytes(B, K, V) bytes, as sv_verify_batch.
+ * Rows may appear in any order and need not be contiguous per request beyond each request's own
+ * run; rows no request uses are never read.
+ * Returns SV_OK, SV_ERR_INVALID_ARG (B, K, V, dtype, a NULL required pointer, n_target_rows < 1,
+ * n_draft_rows < 0, or draft_logits NULL with n_draft_rows > 0; nothing launched),
+ * SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE or SV_ERR_HIP, as sv_verify_batch.
+ */
+int sv_verify_ragged(const void* target_logits, const void* draft_logits, int dtype, int B,
+                     int K, int V, int64_t n_target_rows, int64_t n_draft_rows,
+                     const int32_t* target_row_start, const int32_t* draft_row_start,
+                     const int32_t* num_draft, const float* temperature,
+                     const int32_t* draft_tokens, const float* uniforms,
+                     const float* residual_uniform, int32_t* accepted_len, int32_t* committed,
+                     float* target_prob, float* draft_prob, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
 /* Read probe (a measurement aid, not a step of the method): the plainest stream over a device
  * buffer, so that the row stream can be compared with the read bandwidth this device reaches.
  * `groups` work-groups of 256 threads read every 16-byte word of data[0, bytes) once with

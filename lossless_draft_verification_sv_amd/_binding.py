@@ -58,6 +58,10 @@ def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
         lib.sv_verify_batch.restype = i32
         lib.sv_verify_greedy.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
         lib.sv_verify_greedy.restype = i32
+        i64 = ctypes.c_int64
+        lib.sv_verify_ragged.argtypes = [vp, vp, i32, i32, i32, i32, i64, i64, vp, vp, vp, vp,
+                                         vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.sv_verify_ragged.restype = i32
         lib.sv_read_probe.argtypes = [vp, sz, vp, i32, vp]
         lib.sv_read_probe.restype = i32
         _lib = lib
@@ -189,6 +193,58 @@ def sv_verify_greedy(target: torch.Tensor, draft_tokens: torch.Tensor,
         _ptr(target), _dtype_code(target), B, K, V, _ptr(draft_tokens), _ptr(num_draft),
         _ptr(acc), _ptr(com), _ptr(ws), ws.numel(), stream))
     return VerifyOutput(acc, com, None, None)
+
+
+def sv_verify_ragged(target: torch.Tensor, draft: Optional[torch.Tensor],
+                     draft_tokens: torch.Tensor, uniforms: torch.Tensor,
+                     residual_uniform: torch.Tensor, temperature: torch.Tensor,
+                     num_draft: torch.Tensor, target_row_start: torch.Tensor,
+                     draft_row_start: torch.Tensor,
+                     return_draft_prob: bool = False) -> VerifyOutput:
+    """Flattened, mixed-mode verification on the tensors' GPU (see sv_verify_ragged in
+    include/sv.h).
+
+    target [rows_t, V] and draft [rows_d, V] (or None when no request samples): float32 or
+    bfloat16 logit rows; draft_tokens [B, K] int32; uniforms [B, K] float32; residual_uniform
+    [B] float32; temperature [B] float32 (0 = greedy request); num_draft, target_row_start,
+    draft_row_start [B] int32.
+    """
+    lib = load_library()
+    if target.dim() != 2:
+        raise ValueError("target must be [rows, V]")
+    rows_t, V = target.shape
+    dev = target.device
+    if dev.type != "cuda":
+        raise ValueError("target must be a GPU tensor")
+    _need(target, "target", target.dtype, (rows_t, V), dev)
+    if draft is not None:
+        if draft.dim() != 2:
+            raise ValueError("draft must be [rows, V]")
+        _need(draft, "draft", target.dtype, (draft.shape[0], V), dev)
+    rows_d = 0 if draft is None else draft.shape[0]
+    if draft_tokens.dim() != 2:
+        raise ValueError("draft_tokens must be [B, K]")
+    B, K = draft_tokens.shape
+    _need(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
+    _need(uniforms, "uniforms", torch.float32, (B, K), dev)
+    _need(residual_uniform, "residual_uniform", torch.float32, (B,), dev)
+    _need(temperature, "temperature", torch.float32, (B,), dev)
+    for t, n in ((num_draft, "num_draft"), (target_row_start, "target_row_start"),
+                 (draft_row_start, "draft_row_start")):
+        _need(t, n, torch.int32, (B,), dev)
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    com = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+    tp = torch.empty(B, K, dtype=torch.float32, device=dev)
+    dp = torch.empty(B, K, dtype=torch.float32, device=dev) if return_draft_prob else None
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    nbytes = int(lib.sv_workspace_bytes(B, K, V))
+    ws = _workspace(dev, stream, nbytes)
+    _check(lib.sv_verify_ragged(
+        _ptr(target), _ptr(draft), _dtype_code(target), B, K, V, rows_t, rows_d,
+        _ptr(target_row_start), _ptr(draft_row_start), _ptr(num_draft), _ptr(temperature),
+        _ptr(draft_tokens), _ptr(uniforms), _ptr(residual_uniform), _ptr(acc), _ptr(com),
+        _ptr(tp), _ptr(dp), _ptr(ws), ws.numel(), stream))
+    return VerifyOutput(acc, com, tp, dp)
 
 
 def sv_read_probe(data: torch.Tensor, groups: int = 2048) -> torch.Tensor:

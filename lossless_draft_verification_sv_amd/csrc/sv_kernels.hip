@@ -457,26 +457,80 @@ struct SoftmaxAcc {
   }
 };
 
-// Running argmax over elements in ascending index order; the first maximum is kept.
+// Running argmax over elements in ascending index order; the first maximum is kept. A round's
+// maximum m is taken first; only when it beats the running best is the round searched for the
+// first element equal to m (the same answer as a strict-greater scan: the elements before it are
+// smaller; NaN never compares greater or equal, as in the scan).
 template <int E>
 struct ArgmaxAcc {
   float best;
   int idx;
   template <int N, class A, class Bv>
   __device__ __forceinline__ void consume(const A& f, const Bv&, int g) {
+    float m = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < N; ++j) {
-      const int base = (g + j * kBlock) * E;
+    for (int j = 0; j < N; ++j)
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        if (f[j][e] > best) {
-          best = f[j][e];
-          idx = base + e;
-        }
-      }
+      for (int e = 0; e < E; ++e) m = fmaxf(m, f[j][e]);
+    if (m > best) {
+      int found = INT_MAX;
+#pragma unroll
+      for (int j = N - 1; j >= 0; --j)
+#pragma unroll
+        for (int e = E - 1; e >= 0; --e)
+          if (f[j][e] == m) found = (g + j * kBlock) * E + e;
+      best = m;
+      idx = found;
     }
   }
 };
+
+__device__ __forceinline__ void merge_argmax(float& v, int& i, float v2, int i2) {
+  if (v2 > v || (v2 == v && i2 < i)) {
+    v = v2;
+    i = i2;
+  }
+}
+
+// (value, index) of the whole wave merged, wave-uniform.
+__device__ __forceinline__ void wave_merge_argmax(float& v, int& i) {
+#define SV_ARGMAX_STEP(CTRL, ROWS)                          \
+  merge_argmax(v, i, dpp_f32<CTRL, ROWS>(v, -INFINITY), \
+               (int)dpp_u32<CTRL, ROWS>((uint32_t)i, (uint32_t)INT_MAX))
+  SV_SCAN_STEPS(SV_ARGMAX_STEP);
+#undef SV_ARGMAX_STEP
+  v = lane_f32(v, 63);
+  i = (int)lane_u32((uint32_t)i, 63);
+}
+
+// Argmax partial of groups [g0, g1) of one row by the whole group: (value bits, index) of the
+// first maximum, published as two tagged words at st. Each thread visits its elements in
+// ascending index order and keeps the first maximum; the merges prefer the lower index.
+template <typename T, bool VEC>
+__device__ void argmax_chunk(const T* row, int g0, int g1, uint64_t* st, uint32_t tag) {
+  constexpr int E = Rows<T, VEC>::E;
+  ArgmaxAcc<E> acc{-INFINITY, INT_MAX};
+  // eight-element groups (bf16) hold twice the values per load: half the loads per round keep
+  // the unpacked round within the register budget of the other paths
+  stream_groups<T, VEC, (E == 8 ? kUnroll / 2 : kUnroll), false>(row, row, g0, g1, acc);
+  float best = acc.best;
+  int bi = acc.idx;
+  wave_merge_argmax(best, bi);
+  __shared__ float sv[kWaves];
+  __shared__ int si[kWaves];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    sv[wave] = best;
+    si[wave] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kWaves; ++w) merge_argmax(best, bi, sv[w], si[w]);
+    publish(st, tag, __float_as_uint(best));
+    publish(st + 1, tag, (uint32_t)bi);
+  }
+}
+
 
 // ---------------------------------------------------------------------------------------------
 // Sampling mode.
@@ -499,14 +553,63 @@ struct SampleArgs {
   int32_t* committed;
   float* target_prob;
   float* draft_prob;
+  // Flattened, mixed calls only:
+  const int32_t* t_start;  // [B] first row of request b in the flat target array
+  const int32_t* d_start;  // [B] first row of request b in the flat draft array
+  long n_trows, n_drows;   // rows of the flat arrays
+  const float* temps;      // [B] temperature of request b; 0 makes it a greedy request
 };
+
+constexpr double kLog2e = 1.4426950408889634074;
+constexpr double kTauMin = kLog2e / 2097152.0;  // smallest sampling temperature: c <= 2^21
+constexpr int32_t kBadRequest = -3;             // accepted_len of an invalid request
+
+// What every group of request b needs: k_b, its first target and draft rows, the logit scale
+// c = log2(e) / temperature (fp32), and, in flattened mixed calls (GEN), whether it is a greedy
+// request or an invalid one (rows outside the flat arrays, k_b outside [0, K], temperature
+// negative, not finite or below kTauMin): an invalid request reads nothing.
+template <typename T>
+struct Req {
+  int k;
+  bool greedy, bad;
+  float c;
+  const T* t0;
+  const T* d0;
+};
+
+template <typename T, bool GEN>
+__device__ __forceinline__ Req<T> request_of(const SampleArgs& a, int b) {
+  Req<T> q;
+  const size_t V = a.V;
+  if (!GEN) {
+    q.k = clamp_k(a.num_draft, b, a.K);
+    q.greedy = q.bad = false;
+    q.c = a.c32;
+    q.t0 = static_cast<const T*>(a.target) + (size_t)b * (a.K + 1) * V;
+    q.d0 = static_cast<const T*>(a.draft) + (size_t)b * a.K * V;
+    return q;
+  }
+  const int k = a.num_draft[b];
+  const float tau = a.temps[b];
+  const long ts = a.t_start[b], ds = a.d_start[b];
+  q.greedy = tau == 0.0f;
+  bool ok = k >= 0 && k <= a.K && (q.greedy || ((double)tau >= kTauMin && tau < INFINITY));
+  ok = ok && ts >= 0 && ts + k + 1 <= a.n_trows;
+  if (!q.greedy && k > 0) ok = ok && ds >= 0 && ds + k <= a.n_drows;
+  q.bad = !ok;
+  q.k = ok ? k : 0;
+  q.c = (ok && !q.greedy) ? (float)(kLog2e / (double)tau) : 0.0f;
+  q.t0 = static_cast<const T*>(a.target) + (ok ? (size_t)ts * V : 0);
+  q.d0 = static_cast<const T*>(a.draft) + ((ok && !q.greedy && k > 0) ? (size_t)ds * V : 0);
+  return q;
+}
 
 // Row-stat group wg = (b * (2K+1) + slot) * C + c. Row slot s <= K is target row s, slot K+1+d
 // is draft row d. Unused rows (s > k_b, d >= k_b) return at once without a read.
 // Publishes stats[b][s][c] = (o, sum) with sum = sum_v 2^(fma(z_v, c32, -o)), and, for target
 // slots i < k_b and draft slots i < k_b, the group whose chunk holds the draft token x_i
 // publishes its logit in gath[b][i][0] (target row i) or gath[b][i][1] (draft row i).
-template <typename T, bool VEC>
+template <typename T, bool VEC, bool GEN>
 __device__ void row_stat_group(const SampleArgs& a, long wg) {
   constexpr int E = Rows<T, VEC>::E;
   const int K = a.K, V = a.V, C = a.C;
@@ -515,24 +618,32 @@ __device__ void row_stat_group(const SampleArgs& a, long wg) {
   const long rs = wg / C;
   const int slot = (int)(rs % NR);
   const int b = (int)(rs / NR);
-  const int k = clamp_k(a.num_draft, b, K);
+  const Req<T> q = request_of<T, GEN>(a, b);
+  if (GEN && q.bad) return;
+  const int k = q.k;
+  const int G = VEC ? V / E : V;
+  const int g0 = (int)((long)G * c / C), g1 = (int)((long)G * (c + 1) / C);
+  if (GEN && q.greedy) {  // greedy request: argmax partials of target rows 0..k, no draft rows
+    if (slot > k) return;
+    argmax_chunk<T, VEC>(q.t0 + (size_t)slot * V, g0, g1,
+                         a.stats + (((size_t)b * NR + slot) * C + c) * 2, a.tag);
+    return;
+  }
   const T* row;
   int tslot;  // draft slot whose logit this row provides, or -1 (the extra-draw row)
   int gidx;   // 0: the logit is a target logit, 1: a draft logit
   if (slot <= K) {
     if (slot > k) return;
-    row = static_cast<const T*>(a.target) + ((size_t)b * (K + 1) + slot) * (size_t)V;
+    row = q.t0 + (size_t)slot * V;
     tslot = slot < k ? slot : -1;
     gidx = 0;
   } else {
     const int d = slot - K - 1;
     if (d >= k) return;
-    row = static_cast<const T*>(a.draft) + ((size_t)b * K + d) * (size_t)V;
+    row = q.d0 + (size_t)d * V;
     tslot = d;
     gidx = 1;
   }
-  const int G = VEC ? V / E : V;
-  const int g0 = (int)((long)G * c / C), g1 = (int)((long)G * (c + 1) / C);
 
   if (threadIdx.x == 0 && tslot >= 0) {
     // a token outside the vocabulary has no logit: chunk 0 publishes a placeholder instead, so
@@ -544,7 +655,7 @@ __device__ void row_stat_group(const SampleArgs& a, long wg) {
               valid ? __float_as_uint(Rows<T, VEC>::at(row, x)) : 0u);
   }
 
-  SoftmaxAcc<E> acc{a.c32, -FLT_MAX, 0.0f, 0.0f};
+  SoftmaxAcc<E> acc{q.c, -FLT_MAX, 0.0f, 0.0f};
   stream_groups<T, VEC, kUnroll, false>(row, row, g0, g1, acc);
   float o = acc.o, s = acc.s0 + acc.s1;
 
@@ -871,18 +982,80 @@ __device__ __forceinline__ void row_norm(const uint64_t* st, int C, float& O, do
   }
 }
 
+// Greedy request inside a mixed call, by its chunk-0 draw group: waits for the argmax partials of
+// target rows 0..k, merges them per row (lane i: row i; lane 0 also row 64 when k = 64; the
+// lowest index among equal maxima), n = first i < k with x_i != g_i, else k; writes
+// x_0..x_{n-1}, g_n, -1... and probabilities 0.
+__device__ void greedy_request_finish(const SampleArgs& a, int b, int k, uint64_t* g_stage,
+                                      int* g_late) {
+  const int K = a.K, C = a.C, NR = 2 * K + 1;
+  const uint32_t tag = a.tag;
+  const int lane = threadIdx.x & 63;
+  const int nent = (k + 1) * C;  // <= kStageMax by the plan
+  const int xi = lane < k ? a.tokens[(size_t)b * K + lane] : -1;
+  bool late = false;
+  for (int e0 = 0; e0 < nent; e0 += kBlock * 4) {
+    const uint64_t* p[4];
+    bool live[4];
+    uint64_t wv[4], wi[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      int e = e0 + u * kBlock + (int)threadIdx.x;
+      live[u] = e < nent;
+      e = live[u] ? e : nent - 1;
+      p[u] = a.stats + (((size_t)b * NR + e / C) * C + e % C) * 2;  // target slot e / C
+    }
+    late = late || !await4(p, live, tag, wv, wi);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + u * kBlock + (int)threadIdx.x;
+      if (e < nent) g_stage[e] = ((uint64_t)payload(wv[u]) << 32) | payload(wi[u]);
+    }
+  }
+  if (block_any(late, g_late)) {
+    if (threadIdx.x == 0) a.accepted_len[b] = kTimedOut;
+    return;
+  }
+  if (threadIdx.x >= 64) return;
+  auto row_argmax = [&](int r) {
+    float v = -INFINITY;
+    int idx = INT_MAX;
+    for (int c = 0; c < C; ++c) {
+      const uint64_t w = g_stage[r * C + c];
+      merge_argmax(v, idx, __uint_as_float((uint32_t)(w >> 32)), (int)(uint32_t)w);
+    }
+    return idx == INT_MAX ? 0 : idx;  // a row of -inf only: index 0
+  };
+  const int g = lane <= k ? row_argmax(lane) : 0;
+  const int gx = (k == kMaxK && lane == 0) ? row_argmax(kMaxK) : 0;
+  const uint64_t m = __ballot(lane < k && xi != g);
+  const int n = m ? (__ffsll((long long)m) - 1) : k;
+  const int gn = n < 64 ? (int)lane_u32((uint32_t)g, n) : (int)lane_u32((uint32_t)gx, 0);
+  for (int i = lane; i <= K; i += 64) {
+    int v = -1;
+    if (i < n) v = a.tokens[(size_t)b * K + i];
+    else if (i == n) v = gn;
+    a.committed[(size_t)b * (K + 1) + i] = v;
+    if (i < K) {
+      a.target_prob[(size_t)b * K + i] = 0.0f;
+      if (a.draft_prob != nullptr) a.draft_prob[(size_t)b * K + i] = 0.0f;
+    }
+  }
+  if (lane == 0) a.accepted_len[b] = n;
+}
+
 // Draw group j = b * C2 + c2; chunk c2 covers tiles [NT*c2/C2, NT*(c2+1)/C2).
-template <typename T, bool VEC>
+template <typename T, bool VEC, bool GEN>
 __device__ void draw_group(const SampleArgs& a, long j) {
   constexpr int E = Rows<T, VEC>::E;
   const int K = a.K, V = a.V, C = a.C, C2 = a.C2, NT = a.NT;
   const int b = (int)(j / C2), c2 = (int)(j % C2);
   const int NR = 2 * K + 1;
-  const int k = clamp_k(a.num_draft, b, K);
-  const float c32 = a.c32;
+  const Req<T> q = request_of<T, GEN>(a, b);
+  const int k = q.k;
+  const float c32 = q.c;
   const uint32_t tag = a.tag;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-
   // s_buf stages the row-stat partials from its start, and holds tile sums and chunk totals at
   // its end.
   __shared__ double s_buf[kStageMax];
@@ -891,6 +1064,26 @@ __device__ void draw_group(const SampleArgs& a, long j) {
   __shared__ float s_zt[kMaxK], s_zd[kMaxK];
   __shared__ int s_late1[kWaves], s_late2[kWaves];
   uint64_t* stage = reinterpret_cast<uint64_t*>(s_buf);
+
+  if constexpr (GEN) {
+   if (q.bad || q.greedy) {
+    if (c2 != 0) return;
+    if (q.bad) {
+      for (int i = threadIdx.x; i <= K; i += kBlock) {
+        a.committed[(size_t)b * (K + 1) + i] = -1;
+        if (i < K) {
+          a.target_prob[(size_t)b * K + i] = 0.0f;
+          if (a.draft_prob != nullptr) a.draft_prob[(size_t)b * K + i] = 0.0f;
+        }
+      }
+      if (threadIdx.x == 0) a.accepted_len[b] = kBadRequest;
+      return;
+    }
+    greedy_request_finish(a, b, k, stage, s_late1);
+    return;
+   }
+  }
+
 
   // Per-request inputs, read before the wait. Lane i < k of every wave holds slot i.
   const double r = (double)a.residual[b];
@@ -1028,8 +1221,8 @@ __device__ void draw_group(const SampleArgs& a, long j) {
     }
     if (threadIdx.x == 0) a.accepted_len[b] = n;
   }
-  const T* rt = static_cast<const T*>(a.target) + ((size_t)b * (K + 1) + n) * (size_t)V;
-  const T* rd = resid ? static_cast<const T*>(a.draft) + ((size_t)b * K + n) * (size_t)V : rt;
+  const T* rt = q.t0 + (size_t)n * V;
+  const T* rd = resid ? q.d0 + (size_t)n * V : rt;
   const int G = VEC ? V / E : V;
 
   // 5. Tile sums of this chunk (LDS); wave 0 publishes the chunk total for the other groups of
@@ -1109,31 +1302,23 @@ template <typename T, bool VEC>
 __global__ __launch_bounds__(kBlock) void sv_verify_sample(SampleArgs a) {
   const long wg = blockIdx.x;
   const long n_stat = (long)a.B * (2 * a.K + 1) * a.C;
-  if (wg < n_stat) row_stat_group<T, VEC>(a, wg);
-  else draw_group<T, VEC>(a, wg - n_stat);
+  if (wg < n_stat) row_stat_group<T, VEC, false>(a, wg);
+  else draw_group<T, VEC, false>(a, wg - n_stat);
+}
+
+// Flattened, mixed calls: the same grid and groups, each request read through its own rows and
+// temperature.
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kBlock) void sv_verify_ragged_kernel(SampleArgs a) {
+  const long wg = blockIdx.x;
+  const long n_stat = (long)a.B * (2 * a.K + 1) * a.C;
+  if (wg < n_stat) row_stat_group<T, VEC, true>(a, wg);
+  else draw_group<T, VEC, true>(a, wg - n_stat);
 }
 
 // ---------------------------------------------------------------------------------------------
 // Greedy mode: per-chunk argmax (lowest index among equal maxima), then one finishing group per
 // request.
-
-__device__ __forceinline__ void merge_argmax(float& v, int& i, float v2, int i2) {
-  if (v2 > v || (v2 == v && i2 < i)) {
-    v = v2;
-    i = i2;
-  }
-}
-
-// (value, index) of the whole wave merged, wave-uniform.
-__device__ __forceinline__ void wave_merge_argmax(float& v, int& i) {
-#define SV_ARGMAX_STEP(CTRL, ROWS)                          \
-  merge_argmax(v, i, dpp_f32<CTRL, ROWS>(v, -INFINITY), \
-               (int)dpp_u32<CTRL, ROWS>((uint32_t)i, (uint32_t)INT_MAX))
-  SV_SCAN_STEPS(SV_ARGMAX_STEP);
-#undef SV_ARGMAX_STEP
-  v = lane_f32(v, 63);
-  i = (int)lane_u32((uint32_t)i, 63);
-}
 
 struct GreedyArgs {
   const void* target;  // [B][K+1][V]
@@ -1162,27 +1347,7 @@ __device__ void argmax_group(const GreedyArgs& a, long wg) {
   const T* row = static_cast<const T*>(a.target) + ((size_t)b * (K + 1) + slot) * (size_t)V;
   const int G = VEC ? V / E : V;
   const int g0 = (int)((long)G * c / C), g1 = (int)((long)G * (c + 1) / C);
-
-  // Each thread visits its elements in ascending index order and keeps the first maximum.
-  ArgmaxAcc<E> acc{-INFINITY, INT_MAX};
-  stream_groups<T, VEC, kUnroll, false>(row, row, g0, g1, acc);
-  float best = acc.best;
-  int bi = acc.idx;
-  wave_merge_argmax(best, bi);
-  __shared__ float sv[kWaves];
-  __shared__ int si[kWaves];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) {
-    sv[wave] = best;
-    si[wave] = bi;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int w = 1; w < kWaves; ++w) merge_argmax(best, bi, sv[w], si[w]);
-    uint64_t* st = a.gstats + (((size_t)b * NR + slot) * C + c) * 2;
-    publish(st, a.tag, __float_as_uint(best));
-    publish(st + 1, a.tag, (uint32_t)bi);
-  }
+  argmax_chunk<T, VEC>(row, g0, g1, a.gstats + (((size_t)b * NR + slot) * C + c) * 2, a.tag);
 }
 
 template <typename T, bool VEC>
@@ -1316,11 +1481,15 @@ bool rows_vectorisable(const void* a, const void* b, int dtype, int V) {
          ((size_t)V * elem_size(dtype)) % 16 == 0;
 }
 
-template <typename T, bool VEC>
+template <typename T, bool VEC, bool GEN>
 int launch_sample(const SampleArgs& a, long groups, hipStream_t stream) {
-  hipLaunchKernelGGL((sv_verify_sample<T, VEC>), dim3((unsigned)groups), dim3(kBlock), 0, stream,
-                     a);
-  return launch_status("sv_verify_sample");
+  if (GEN)
+    hipLaunchKernelGGL((sv_verify_ragged_kernel<T, VEC>), dim3((unsigned)groups), dim3(kBlock),
+                       0, stream, a);
+  else
+    hipLaunchKernelGGL((sv_verify_sample<T, VEC>), dim3((unsigned)groups), dim3(kBlock), 0,
+                       stream, a);
+  return launch_status(GEN ? "sv_verify_ragged" : "sv_verify_sample");
 }
 
 template <typename T, bool VEC>
@@ -1408,12 +1577,86 @@ int sv_verify_batch(const void* target_logits, const void* draft_logits, int dty
   a.committed = committed;
   a.target_prob = target_prob;
   a.draft_prob = draft_prob;
+  a.t_start = a.d_start = nullptr;
+  a.n_trows = a.n_drows = 0;
+  a.temps = nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool vec = rows_vectorisable(target_logits, draft_logits, dtype, V);
   if (dtype == SV_DTYPE_F32)
-    return vec ? launch_sample<float, true>(a, groups, s) : launch_sample<float, false>(a, groups, s);
-  return vec ? launch_sample<uint16_t, true>(a, groups, s)
-             : launch_sample<uint16_t, false>(a, groups, s);
+    return vec ? launch_sample<float, true, false>(a, groups, s)
+               : launch_sample<float, false, false>(a, groups, s);
+  return vec ? launch_sample<uint16_t, true, false>(a, groups, s)
+             : launch_sample<uint16_t, false, false>(a, groups, s);
+}
+
+int sv_verify_ragged(const void* target_logits, const void* draft_logits, int dtype, int B,
+                     int K, int V, int64_t n_target_rows, int64_t n_draft_rows,
+                     const int32_t* target_row_start, const int32_t* draft_row_start,
+                     const int32_t* num_draft, const float* temperature,
+                     const int32_t* draft_tokens, const float* uniforms,
+                     const float* residual_uniform, int32_t* accepted_len, int32_t* committed,
+                     float* target_prob, float* draft_prob, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int st = check_shape(B, K, V);
+  if (st != SV_OK) return st;
+  if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16)
+    return fail(SV_ERR_INVALID_ARG, "dtype must be SV_DTYPE_F32 or SV_DTYPE_BF16");
+  if (!target_logits || !target_row_start || !draft_row_start || !num_draft || !temperature ||
+      !draft_tokens || !uniforms || !residual_uniform || !accepted_len || !committed ||
+      !target_prob)
+    return fail(SV_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (n_target_rows < 1 || n_draft_rows < 0)
+    return fail(SV_ERR_INVALID_ARG, "n_target_rows must be >= 1 and n_draft_rows >= 0");
+  if (n_draft_rows > 0 && !draft_logits)
+    return fail(SV_ERR_INVALID_ARG, "draft_logits is NULL but n_draft_rows > 0");
+  if ((unsigned long long)n_target_rows * (unsigned long long)V > (1ull << 46) ||
+      (unsigned long long)n_draft_rows * (unsigned long long)V > (1ull << 46))
+    return fail(SV_ERR_UNSUPPORTED, "flat logit arrays too large");
+  const Plan p = make_plan(B, K, V);
+  if (!plan_supported(p)) return fail(SV_ERR_UNSUPPORTED, "vocabulary too large");
+  const Layout L = make_layout(B, K, V, p);
+  st = check_workspace(workspace, workspace_bytes, L.total);
+  if (st != SV_OK) return st;
+  const long n_stat = (long)B * (2 * K + 1) * p.C;
+  const long groups = n_stat + (long)B * p.C2;
+  st = check_grid(groups);
+  if (st != SV_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  SampleArgs a;
+  a.target = target_logits;
+  a.draft = n_draft_rows > 0 ? draft_logits : target_logits;  // never read when empty
+  a.B = B;
+  a.K = K;
+  a.V = V;
+  a.num_draft = num_draft;
+  a.tokens = draft_tokens;
+  a.uniforms = uniforms;
+  a.residual = residual_uniform;
+  a.c32 = 0.0f;  // per request
+  a.C = p.C;
+  a.C2 = p.C2;
+  a.NT = p.NT;
+  a.tag = next_tag();
+  a.stats = reinterpret_cast<uint64_t*>(ws + L.stats);
+  a.gath = reinterpret_cast<uint64_t*>(ws + L.gath);
+  a.ctot = reinterpret_cast<uint64_t*>(ws + L.ctot);
+  a.accepted_len = accepted_len;
+  a.committed = committed;
+  a.target_prob = target_prob;
+  a.draft_prob = draft_prob;
+  a.t_start = target_row_start;
+  a.d_start = draft_row_start;
+  a.n_trows = (long)n_target_rows;
+  a.n_drows = (long)n_draft_rows;
+  a.temps = temperature;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool vec = rows_vectorisable(target_logits, a.draft, dtype, V);
+  if (dtype == SV_DTYPE_F32)
+    return vec ? launch_sample<float, true, true>(a, groups, s)
+               : launch_sample<float, false, true>(a, groups, s);
+  return vec ? launch_sample<uint16_t, true, true>(a, groups, s)
+             : launch_sample<uint16_t, false, true>(a, groups, s);
 }
 
 int sv_verify_greedy(const void* target_logits, int dtype, int B, int K, int V,

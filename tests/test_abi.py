@@ -122,6 +122,43 @@ def test_greedy_rejects_invalid_arguments(lib, kw, status):
     assert sv.sv_last_error() != ""
 
 
+def call_ragged(lib, **kw):
+    args = dict(target=FAKE, draft=FAKE, dtype=sv.SV_DTYPE_BF16, B=2, K=4, V=1000, rows_t=10,
+                rows_d=8, t_start=FAKE, d_start=FAKE, num_draft=FAKE, temperature=FAKE,
+                tokens=FAKE, uniforms=FAKE, residual=FAKE, acc=FAKE, com=FAKE, tp=FAKE, dp=None,
+                ws=WS, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return lib.sv_verify_ragged(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), sv.SV_ERR_INVALID_ARG),
+    (dict(K=65), sv.SV_ERR_INVALID_ARG),
+    (dict(V=0), sv.SV_ERR_INVALID_ARG),
+    (dict(dtype=3), sv.SV_ERR_INVALID_ARG),
+    (dict(target=None), sv.SV_ERR_INVALID_ARG),
+    (dict(t_start=None), sv.SV_ERR_INVALID_ARG),
+    (dict(d_start=None), sv.SV_ERR_INVALID_ARG),
+    (dict(num_draft=None), sv.SV_ERR_INVALID_ARG),
+    (dict(temperature=None), sv.SV_ERR_INVALID_ARG),
+    (dict(tokens=None), sv.SV_ERR_INVALID_ARG),
+    (dict(uniforms=None), sv.SV_ERR_INVALID_ARG),
+    (dict(residual=None), sv.SV_ERR_INVALID_ARG),
+    (dict(acc=None), sv.SV_ERR_INVALID_ARG),
+    (dict(com=None), sv.SV_ERR_INVALID_ARG),
+    (dict(tp=None), sv.SV_ERR_INVALID_ARG),
+    (dict(rows_t=0), sv.SV_ERR_INVALID_ARG),
+    (dict(rows_d=-1), sv.SV_ERR_INVALID_ARG),
+    (dict(draft=None), sv.SV_ERR_INVALID_ARG),
+    (dict(ws=None), sv.SV_ERR_WORKSPACE),
+    (dict(ws=WS + 8), sv.SV_ERR_WORKSPACE),
+    (dict(ws_bytes=32), sv.SV_ERR_WORKSPACE),
+])
+def test_ragged_rejects_invalid_arguments(lib, kw, status):
+    assert call_ragged(lib, **kw) == status
+    assert sv.sv_last_error() != ""
+
+
 def test_workspace_size_is_exactly_enough(lib):
     need = sv.sv_workspace_bytes(2, 4, 1000)
     assert call_batch(lib, ws_bytes=need - 1) == sv.SV_ERR_WORKSPACE

@@ -1,0 +1,143 @@
+"""Flattened, mixed-mode verification (sv_verify_ragged) against the fp64 oracle (GPU).
+
+Mixed batches hold greedy requests (temperature 0) and sampling requests at several
+temperatures, each with its own verify length, read from packed rows in a shuffled order.
+Greedy requests must match bit for bit; sampling requests to the parity bar of the padded
+path. On the same requests the flattened call must also give exactly what the padded entry
+points give (same plan, same arithmetic), and invalid requests must be flagged without
+disturbing the others.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+import torch  # noqa: E402
+
+import lossless_draft_verification_sv_amd as sv  # noqa: E402
+import oracle  # noqa: E402
+from tests.gpu_util import PROB_TOL, run_greedy, run_sample, say, to_dev  # noqa: E402
+from tests.test_oracle_pins import golden_flat_batch  # noqa: E402
+from workloads import HEAVY, MIXED, flatten, generate  # noqa: E402
+
+
+def run_ragged(target, draft, tokens, uniforms, residual, temps, num_draft, ts, ds):
+    out = sv.sv_verify_ragged(to_dev(target), to_dev(draft), to_dev(tokens), to_dev(uniforms),
+                              to_dev(residual), to_dev(np.asarray(temps, np.float32)),
+                              to_dev(np.asarray(num_draft, np.int32)),
+                              to_dev(np.asarray(ts, np.int32)), to_dev(np.asarray(ds, np.int32)),
+                              return_draft_prob=True)
+    torch.cuda.synchronize()
+    return (out.accepted_len.cpu().numpy(), out.committed.cpu().numpy(),
+            out.target_prob.cpu().numpy(), out.draft_prob.cpu().numpy())
+
+
+def run_flat(f):
+    return run_ragged(f.target, f.draft, f.tokens, f.uniforms, f.residual, f.temperatures,
+                      f.num_draft, f.target_row_start, f.draft_row_start)
+
+
+def check_ragged_parity(name, f, requests=None):
+    w = f.workload
+    acc, com, tp, dp = run_flat(f)
+    ref = oracle.verify_ragged(f.target, f.draft, w.dtype, f.tokens, f.uniforms, f.residual,
+                               f.temperatures, f.num_draft, f.target_row_start,
+                               f.draft_row_start, requests=requests)
+    idx = np.arange(w.B) if requests is None else np.asarray(requests)
+    amb = ref.ambiguous[idx]
+    greedy = idx[f.temperatures[idx] == 0]
+    samp = idx[(f.temperatures[idx] > 0) & ~amb]
+    tp_err = float(np.max(np.abs(tp[idx] - ref.target_prob[idx])))
+    dp_err = float(np.max(np.abs(dp[idx] - ref.draft_prob[idx])))
+    say(f"[gpu] ragged {name}: {len(idx)} requests ({len(greedy)} greedy, {int(amb.sum())} "
+        f"ambiguous), max |dp| {tp_err:.2e} / {dp_err:.2e}")
+    assert tp_err <= PROB_TOL and dp_err <= PROB_TOL, name
+    assert np.array_equal(acc[greedy], ref.accepted_len[greedy]), name
+    assert np.array_equal(com[greedy], ref.committed[greedy]), name
+    assert np.array_equal(acc[samp], ref.accepted_len[samp]), name
+    assert np.array_equal(com[samp], ref.committed[samp]), name
+    return acc, com, tp, dp
+
+
+SMALL = [
+    # (B, K, V, dtype, seed)
+    (12, 6, 4096, "f32", 1),  # vector rows
+    (10, 5, 4099, "f32", 2),  # odd V: scalar path
+    (16, 8, 16400, "bf16", 3),  # vector bf16, several chunks per row
+    (9, 16, 3001, "bf16", 4),  # scalar bf16, K = 16
+    (6, 64, 520, "f32", 5),  # K = 64: lane 0 also holds row 64
+]
+
+
+@pytest.mark.parametrize("B,K,V,dtype,seed", SMALL)
+def test_mixed_flat_small(B, K, V, dtype, seed):
+    w = MIXED.replace(name=f"mixed_B{B}_K{K}_V{V}_{dtype}", B=B, K=K, V=V, dtype=dtype,
+                      seed=4000 + seed)
+    inp = generate(w)
+    order = np.random.default_rng(seed).permutation(B)
+    check_ragged_parity(w.name, flatten(inp, order))
+
+
+def test_flat_equals_padded_bitwise():
+    """All-sampling ragged batch: flattened and padded calls give identical outputs."""
+    w = HEAVY.replace(name="heavy_small", B=24, K=8, V=40000, seed=4101)
+    inp = generate(w)
+    f = flatten(inp, np.random.default_rng(7).permutation(w.B))
+    acc, com, tp, dp = run_flat(f)
+    a2, c2, t2, d2 = run_sample(inp.target, inp.draft, inp.tokens, inp.uniforms, inp.residual,
+                                w.temperature, inp.num_draft)
+    assert np.array_equal(acc, a2) and np.array_equal(com, c2)
+    assert np.array_equal(tp.view(np.uint32), t2.view(np.uint32))
+    assert np.array_equal(dp.view(np.uint32), d2.view(np.uint32))
+
+
+def test_flat_all_greedy_equals_greedy_entry_point():
+    w = HEAVY.replace(name="heavy_greedy_small", B=20, K=8, V=30000, mode="greedy", seed=4102)
+    inp = generate(w)
+    f = flatten(inp, np.random.default_rng(8).permutation(w.B))
+    acc, com, tp, _ = run_flat(f)
+    a2, c2 = run_greedy(inp.target, inp.tokens, inp.num_draft)
+    assert np.array_equal(acc, a2) and np.array_equal(com, c2)
+    assert not tp.any()
+
+
+def test_invalid_requests_are_flagged_and_isolated():
+    w = MIXED.replace(name="mixed_invalid", B=10, K=5, V=3000, dtype="f32", seed=4103)
+    f = flatten(generate(w))
+    ref_acc, ref_com, _, _ = check_ragged_parity("mixed_invalid_clean", f)
+    bad = {1: ("target_row_start", -1), 2: ("target_row_start", f.target.shape[0] - 1),
+           3: ("temperatures", -1.0), 5: ("temperatures", np.nan), 6: ("num_draft", 6),
+           7: ("temperatures", 1e-9)}
+    samp = [b for b in range(w.B) if f.temperatures[b] > 0 and f.num_draft[b] > 0 and b not in bad]
+    bad[samp[0]] = ("draft_row_start", f.draft.shape[0])
+    arrays = {k: getattr(f, k).copy() for k in ("target_row_start", "draft_row_start",
+                                                  "num_draft", "temperatures")}
+    for b, (key, val) in bad.items():
+        arrays[key][b] = val
+    acc, com, tp, dp = run_ragged(f.target, f.draft, f.tokens, f.uniforms, f.residual,
+                                  arrays["temperatures"], arrays["num_draft"],
+                                  arrays["target_row_start"], arrays["draft_row_start"])
+    for b in range(w.B):
+        if b in bad:
+            assert acc[b] == oracle.RAGGED_INVALID and np.all(com[b] == -1), b
+            assert not tp[b].any() and not dp[b].any(), b
+        else:
+            assert acc[b] == ref_acc[b] and np.array_equal(com[b], ref_com[b]), b
+
+
+def test_golden_examples_as_one_flat_batch_on_gpu():
+    batch, expected = golden_flat_batch()
+    acc, com, tp, dp = run_ragged(batch["target_flat"], batch["draft_flat"], batch["tokens"],
+                                  batch["uniforms"].astype(np.float32),
+                                  batch["residual"].astype(np.float32), batch["temperatures"],
+                                  batch["num_draft"], batch["target_row_start"],
+                                  batch["draft_row_start"])
+    for b, (n, c, t, d) in enumerate(expected):
+        assert acc[b] == n and com[b].tolist() == c, b
+        assert np.allclose(tp[b], t, atol=PROB_TOL) and np.allclose(dp[b], d, atol=PROB_TOL), b
+
+
+def test_full_mixed_B256_K16_bf16_sampled_requests():
+    inp = generate(MIXED)
+    f = flatten(inp)
+    check_ragged_parity(MIXED.name, f, requests=list(range(0, MIXED.B, 7)))

@@ -70,3 +70,31 @@ def test_sampled_tokens_follow_the_draft_distribution():
     expect = np.sum(p * p, axis=1)
     z = (probs.mean() - expect.mean()) / (probs.std() / np.sqrt(w.B))
     assert abs(z) < 4
+
+
+def test_mixed_workload_and_flatten():
+    from workloads import MIXED, flatten
+
+    w = MIXED.replace(B=9, K=5, V=300, seed=12)
+    inp = generate(w)
+    assert list(inp.temperatures) == [w.temperature_of(b) for b in range(w.B)]
+    for b in range(w.B):  # greedy requests propose the argmax of their draft rows
+        if inp.temperatures[b] == 0:
+            k = inp.k_of(b)
+            d = bf16_bits_to_f32(inp.draft[b, :k]).astype(np.float64)
+            assert list(inp.tokens[b, :k]) == list(np.argmax(d, axis=1))
+    order = [4, 2, 8, 0, 1, 7, 3, 6, 5]
+    f = flatten(inp, order)
+    ks = [inp.k_of(b) for b in range(w.B)]
+    assert f.target.shape[0] == sum(k + 1 for k in ks)
+    assert f.draft.shape[0] == sum(k for b, k in enumerate(ks) if inp.temperatures[b] > 0)
+    for b in range(w.B):
+        k = ks[b]
+        assert np.array_equal(f.target[f.target_row_start[b]:f.target_row_start[b] + k + 1],
+                              inp.target[b, :k + 1])
+        if inp.temperatures[b] > 0:
+            assert np.array_equal(f.draft[f.draft_row_start[b]:f.draft_row_start[b] + k],
+                                  inp.draft[b, :k])
+    # requests are packed in the order given
+    starts = [f.target_row_start[b] for b in order]
+    assert starts == sorted(starts)

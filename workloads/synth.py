@@ -5,11 +5,12 @@ uniforms, the residual uniform and the per-request number of drafts to verify. I
 of the verification arithmetic (no softmax, no acceptance test, no residual sampling), so that
 the oracle and the GPU path can both consume its output without sharing any of the method.
 
-Draft tokens for sampling workloads are drawn from softmax(d / tau) with the exponential-race
+Draft tokens for sampling requests are drawn from softmax(d / tau) with the exponential-race
 form of the Gumbel-max construction: x = argmax_v (d_v / tau - log E_v), E_v ~ Exp(1) i.i.d.
 Since -log E_v is standard Gumbel, x has exactly the categorical law softmax(d / tau) of the
-stored (already rounded) draft row. Greedy workloads take x = argmax_v d_v (lowest index on
-ties), the proposal a greedy drafter makes.
+stored (already rounded) draft row. Greedy requests take x = argmax_v d_v (lowest index on
+ties), the proposal a greedy drafter makes. In a mixed workload request b has temperature
+temperatures[b % len(temperatures)], 0 marking a greedy request.
 
 Shapes and value distributions stand in for the pages' workloads (no dataset is used):
   * vocabulary 151936, the size of the Qwen3-8B target used for the single-H100 comparison in
@@ -19,12 +20,14 @@ Shapes and value distributions stand in for the pages' workloads (no dataset is 
   * one request in flight vs 64 in flight vs a heavily loaded batch (DSpark review, section 6);
   * per-request verify lengths that differ inside one batch (DSpark review, 4.2.2 and 5.3);
   * later draft slots agreeing less with the target ("suffix decay", DSpark review 3.2 and
-    "From draft-then-verify to DSpark", DFlash section).
+    "From draft-then-verify to DSpark", DFlash section);
+  * batches flattened to the rows each request uses, with greedy and sampling requests mixed
+    (DSpark review 4.2.2; "Bringing DSpark to vLLM Metal", greedy-only serving).
 
 Randomness: every request b of a workload draws from its own generator
 numpy.random.default_rng(SeedSequence([seed, b])), in this fixed order:
   1. target normals [K+1, V] (float32);  2. spike indices [K+1] (if the workload has a spike);
-  3. draft noise [K, V] (float32);       4. draft-token exponentials [K, V] (sampling only);
+  3. draft noise [K, V] (float32);       4. draft-token exponentials [K, V] (sampling requests);
   5. per-slot uniforms u [K] (float32);  6. residual uniform r (float32);
   7. the number of drafts k_b (ragged workloads only).
 Noise is added in float32; bf16 storage rounds to nearest, ties to even.
@@ -51,17 +54,24 @@ class Workload:
     V: int
     dtype: str  # "f32" or "bf16": storage type of both logit tensors
     temperature: float
-    mode: str  # "sample" or "greedy"
+    mode: str  # "sample", "greedy" or "mixed" (per-request temperatures, 0 = greedy)
     target_sigma: float
     spike: float  # added to one random vocabulary entry per target row; 0 = none
     draft_sigma: Sequence[float]  # per draft slot, length K
     identical_even: bool = False  # even requests: draft rows = target rows bitwise
     ragged: bool = False  # k_b ~ U{1..K}; rows past k_b are NaN-filled
     seed: int = 0
+    temperatures: Sequence[float] = ()  # mixed mode: request b has temperatures[b % len]
 
     @property
     def rows_per_request(self) -> int:
         return 2 * self.K + 1 if self.mode == "sample" else self.K + 1
+
+    def temperature_of(self, b: int) -> float:
+        """Temperature of request b: 0 for a greedy request."""
+        if self.mode == "mixed":
+            return float(self.temperatures[b % len(self.temperatures)])
+        return 0.0 if self.mode == "greedy" else float(self.temperature)
 
     def replace(self, **kw) -> "Workload":
         if "K" in kw and "draft_sigma" not in kw:
@@ -93,7 +103,12 @@ HEAVY = Workload("heavy_ragged_sample_B256_K16_V151936_bf16", 256, 16, QWEN3_VOC
 GREEDY = Workload("greedy_B512_K8_V151936_f32", 512, 8, QWEN3_VOCAB, "f32", 1.0, "greedy",
                   3.0, 12.0, (1.0,) * 8, seed=1005)
 
-WORKLOADS = {w.name: w for w in (TINY, INTERACTIVE, BATCHED, HEAVY, GREEDY)}
+# Heavy ragged load with greedy and sampling requests mixed, verified from flattened rows.
+MIXED = Workload("mixed_flat_B256_K16_V151936_bf16", 256, 16, QWEN3_VOCAB, "bf16", 1.0, "mixed",
+                 3.0, 12.0, _ramp(0.5, 3.0, 16), ragged=True, seed=1006,
+                 temperatures=(0.0, 0.7, 1.0, 1.3))
+
+WORKLOADS = {w.name: w for w in (TINY, INTERACTIVE, BATCHED, HEAVY, GREEDY, MIXED)}
 BY_NUMBER = {1: TINY, 2: INTERACTIVE, 3: BATCHED, 4: HEAVY, 5: GREEDY}
 
 
@@ -140,6 +155,7 @@ class Inputs:
     uniforms: np.ndarray
     residual: np.ndarray
     num_draft: Optional[np.ndarray]
+    temperatures: Optional[np.ndarray] = None  # [B] float32, mixed workloads
 
     @property
     def B(self):
@@ -181,9 +197,10 @@ def _gen_request(w: Workload, b: int, out: Inputs) -> None:
     else:
         d_st = _stored(t32[:K] + noise, w.dtype)
     d64 = _as_f64(d_st, w.dtype)
-    if w.mode == "sample":
+    tau = w.temperature_of(b)
+    if tau > 0.0:
         e = rng.standard_exponential((K, V))  # float64: never exactly 0
-        keys = d64 / w.temperature - np.log(e)
+        keys = d64 / tau - np.log(e)
         x = np.argmax(keys, axis=1).astype(np.int32)
     else:
         x = np.argmax(d64, axis=1).astype(np.int32)
@@ -204,6 +221,8 @@ def _gen_request(w: Workload, b: int, out: Inputs) -> None:
     out.residual[b] = r
     if out.num_draft is not None:
         out.num_draft[b] = k
+    if out.temperatures is not None:
+        out.temperatures[b] = tau
 
 
 def generate(w: Workload, threads: Optional[int] = None) -> Inputs:
@@ -212,11 +231,12 @@ def generate(w: Workload, threads: Optional[int] = None) -> Inputs:
     out = Inputs(
         workload=w,
         target=np.empty((w.B, w.K + 1, w.V), dtype=st),
-        draft=np.empty((w.B, w.K, w.V), dtype=st) if w.mode == "sample" else None,
+        draft=np.empty((w.B, w.K, w.V), dtype=st) if w.mode != "greedy" else None,
         tokens=np.empty((w.B, w.K), dtype=np.int32),
         uniforms=np.empty((w.B, w.K), dtype=np.float32),
         residual=np.empty((w.B,), dtype=np.float32),
         num_draft=np.empty((w.B,), dtype=np.int32) if w.ragged else None,
+        temperatures=np.empty((w.B,), dtype=np.float32) if w.mode == "mixed" else None,
     )
     if threads is None:
         threads = min(16, len(os.sched_getaffinity(0)))
@@ -227,3 +247,48 @@ def generate(w: Workload, threads: Optional[int] = None) -> Inputs:
         with ThreadPoolExecutor(max_workers=threads) as ex:
             list(ex.map(lambda b: _gen_request(w, b, out), range(w.B)))
     return out
+
+
+@dataclasses.dataclass
+class FlatInputs:
+    """A workload with its logit rows packed: request b's k_b+1 target rows start at
+    target_row_start[b] of target [rows_t, V], and, for a sampling request, its k_b draft rows at
+    draft_row_start[b] of draft [rows_d, V] (None when no request samples). Greedy requests have
+    temperature 0 and no draft rows. Small per-request arrays stay [B, K] / [B]."""
+
+    workload: Workload
+    target: np.ndarray
+    draft: Optional[np.ndarray]
+    target_row_start: np.ndarray
+    draft_row_start: np.ndarray
+    num_draft: np.ndarray
+    temperatures: np.ndarray
+    tokens: np.ndarray
+    uniforms: np.ndarray
+    residual: np.ndarray
+
+
+def flatten(inp: Inputs, order: Optional[Sequence[int]] = None) -> FlatInputs:
+    """Pack the rows each request uses, requests in `order` (default: ascending)."""
+    w = inp.workload
+    B = w.B
+    order = list(range(B)) if order is None else list(order)
+    ks = np.array([inp.k_of(b) for b in range(B)], dtype=np.int32)
+    taus = (inp.temperatures.astype(np.float32) if inp.temperatures is not None else
+            np.array([w.temperature_of(b) for b in range(B)], dtype=np.float32))
+    ts = np.zeros(B, np.int32)
+    ds = np.zeros(B, np.int32)
+    nt = nd = 0
+    for b in order:
+        ts[b], nt = nt, nt + ks[b] + 1
+        ds[b] = nd
+        if taus[b] > 0:
+            nd += ks[b]
+    target = np.empty((nt, w.V), dtype=inp.target.dtype)
+    draft = np.empty((nd, w.V), dtype=inp.target.dtype) if nd > 0 else None
+    for b in order:
+        target[ts[b]:ts[b] + ks[b] + 1] = inp.target[b, :ks[b] + 1]
+        if taus[b] > 0 and ks[b] > 0:
+            draft[ds[b]:ds[b] + ks[b]] = inp.draft[b, :ks[b]]
+    return FlatInputs(w, target, draft, ts, ds, ks, taus, inp.tokens, inp.uniforms,
+                      inp.residual)
