@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="batched",
-                    help="tiny | interactive | batched | heavy | greedy | mixed | "
+                    help="tiny | interactive | batched | heavy | greedy | mixed | schedule | "
                          "sweep_<mode>_<K>_<B>_<dtype>")
     ap.add_argument("--min-rotation-bytes", type=float, default=1.2e9,
                     help="rotate input copies until at least this many bytes are cycled")
@@ -213,6 +213,72 @@ def read_ceiling(lib, call_bytes, dev, stream):
     return big, same
 
 
+def bench_schedule(args):
+    """The prefix scheduler (sv_schedule_prefix) at B=256, K=16: synthetic confidences and a
+    step-time table measured on this device's verify kernel plus a synthetic target step."""
+    import torch
+
+    import lossless_draft_verification_sv_amd as sv
+    import oracle
+    from lossless_draft_verification_sv_amd.schedule import step_time_table
+    from workloads import QWEN3_VOCAB, schedule_confidences
+
+    B, K = 256, 16
+    conf = schedule_confidences(B, K)
+    dev = torch.device("cuda:0")
+    tab = step_time_table(B, K, QWEN3_VOCAB, "bf16")
+    c_d, t_d = torch.from_numpy(conf).to(dev), torch.from_numpy(tab).to(dev)
+    lib = sv.load_library()
+    out = torch.empty(B, dtype=torch.int32, device=dev)
+    ts = torch.empty(B, dtype=torch.int32, device=dev)
+    ds = torch.empty(B, dtype=torch.int32, device=dev)
+    summ = torch.empty(2, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    argv = (c_d.data_ptr(), B, K, t_d.data_ptr(), tab.shape[0], 0.5, out.data_ptr(),
+            ts.data_ptr(), ds.data_ptr(), summ.data_ptr(), stream.cuda_stream)
+    for _ in range(args.warmup):
+        assert lib.sv_schedule_prefix(*argv) == 0
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        lib.sv_schedule_prefix(*argv)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t_start) * 1e3 / args.steps
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    num = out.cpu().numpy()
+    n_chosen = int(summ[0].item())
+    c0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.schedule_hardware_aware(conf, tab.astype(np.float64))
+        reps += 1
+        if time.perf_counter() - c0 > min(args.cpu_seconds, 5.0) or args.cpu_seconds <= 0:
+            break
+    cpu_s = (time.perf_counter() - c0) / reps
+    result = {
+        "metric": "scheduled draft tokens/s (sv_schedule_prefix, B*K tokens ranked per call)",
+        "value": B * K / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic confidences; step table = measured verify kernel + synthetic target",
+        "config": {"workload": "schedule_B256_K16", "B": B, "K": K,
+                   "table_entries": int(tab.shape[0])},
+        "call_us": {"mean_timed": us},
+        "chosen_tokens": n_chosen, "mean_num_draft": float(num.mean()),
+        "roofline": {"bound": "latency", "kernel": "sv_schedule_kernel", "achieved": us,
+                     "peak": None, "unit": "us per call", "frac": None, "traffic": None},
+        "cpu_baseline": {"value": B * K / cpu_s, "unit": "tokens/s", "cores": 1,
+                         "kind": "oracle", "sample": f"{reps} full schedules, fp64 python"},
+    }
+    print(json.dumps(result), flush=True)
+    if args.out:
+        with open(args.out, "a") as f:
+            f.write(json.dumps(result) + "\n")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -225,6 +291,8 @@ def main():
     import lossless_draft_verification_sv_amd as sv
     from workloads import flatten, generate
 
+    if args.workload == "schedule":
+        return bench_schedule(args)
     w = pick_workload(args.workload)
     inp = generate(w)
     # the pooled oracle runs first, before this process touches the GPU

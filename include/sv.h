@@ -156,6 +156,33 @@ int sv_verify_ragged(const void* target_logits, const void* draft_logits, int dt
                      float* target_prob, float* draft_prob, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/* Confidence-scheduled prefix selection ("DSpark" paper review, 4.2.1 Confidence Head and
+ * 4.2.2 Hardware-Aware Prefix Scheduler): how many draft tokens of each request to verify.
+ * Prefix survival s[b][k] = c[b][0] * ... * c[b][k] (confidences clamped to [0, 1], NaN = 0,
+ * float32 products left to right).
+ *  step_time != NULL (hardware-aware): all B*K draft tokens are ranked by survival (ties: earlier
+ *    position, then lower request); N = 0 .. B*K is chosen to maximise
+ *    (B + sum of the first N ranked survivals) / step_time[B + N]   (fp64 sums; the smallest N
+ *    among equal rates; entries that are not finite and positive are skipped), and request b
+ *    verifies its tokens among the first N (always a prefix).
+ *  step_time == NULL (threshold): request b verifies its drafts up to the first confidence below
+ *    `threshold`.
+ *
+ *  confidence        [B, K] float, device
+ *  step_time         [T] float, device: time of a target step that verifies n tokens, n < T;
+ *                    T >= B + B*K + 1. The units are the caller's.
+ *  num_draft         [B] int32 out (device): k_b
+ *  target_row_start  [B] int32 out or NULL: exclusive sums of k_b + 1 (flattened target rows)
+ *  draft_row_start   [B] int32 out or NULL: exclusive sums of k_b (flattened draft rows)
+ *  summary           [2] float out or NULL: N chosen, and its expected tokens per unit time
+ *                    (0, 0 in threshold mode)
+ *  Limits: 1 <= K <= 64, B*K <= 4096. One work-group; asynchronous on `stream`.
+ * Returns SV_OK, SV_ERR_INVALID_ARG (nothing launched) or SV_ERR_HIP.
+ */
+int sv_schedule_prefix(const float* confidence, int B, int K, const float* step_time, int T,
+                       float threshold, int32_t* num_draft, int32_t* target_row_start,
+                       int32_t* draft_row_start, float* summary, void* stream);
+
 /* Read probe (a measurement aid, not a step of the method): the plainest stream over a device
  * buffer, so that the row stream can be compared with the read bandwidth this device reaches.
  * `groups` work-groups of 256 threads read every 16-byte word of data[0, bytes) once with

@@ -62,6 +62,8 @@ def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
         lib.sv_verify_ragged.argtypes = [vp, vp, i32, i32, i32, i32, i64, i64, vp, vp, vp, vp,
                                          vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.sv_verify_ragged.restype = i32
+        lib.sv_schedule_prefix.argtypes = [vp, i32, i32, vp, i32, f32, vp, vp, vp, vp, vp]
+        lib.sv_schedule_prefix.restype = i32
         lib.sv_read_probe.argtypes = [vp, sz, vp, i32, vp]
         lib.sv_read_probe.restype = i32
         _lib = lib
@@ -245,6 +247,42 @@ def sv_verify_ragged(target: torch.Tensor, draft: Optional[torch.Tensor],
         _ptr(draft_tokens), _ptr(uniforms), _ptr(residual_uniform), _ptr(acc), _ptr(com),
         _ptr(tp), _ptr(dp), _ptr(ws), ws.numel(), stream))
     return VerifyOutput(acc, com, tp, dp)
+
+
+class ScheduleOutput(NamedTuple):
+    num_draft: torch.Tensor  # [B] int32
+    target_row_start: torch.Tensor  # [B] int32
+    draft_row_start: torch.Tensor  # [B] int32
+    summary: torch.Tensor  # [2] float32: N chosen, expected tokens per unit time
+
+
+def sv_schedule_prefix(confidence: torch.Tensor, step_time: Optional[torch.Tensor] = None,
+                       threshold: float = 0.5) -> ScheduleOutput:
+    """Confidence-scheduled prefix selection on the tensor's GPU (see sv_schedule_prefix in
+    include/sv.h). confidence [B, K] float32; step_time [T] float32 (hardware-aware mode) or
+    None (threshold mode)."""
+    lib = load_library()
+    if confidence.dim() != 2:
+        raise ValueError("confidence must be [B, K]")
+    B, K = confidence.shape
+    dev = confidence.device
+    if dev.type != "cuda":
+        raise ValueError("confidence must be a GPU tensor")
+    _need(confidence, "confidence", torch.float32, (B, K), dev)
+    T = 0
+    if step_time is not None:
+        if step_time.dim() != 1:
+            raise ValueError("step_time must be [T]")
+        T = step_time.shape[0]
+        _need(step_time, "step_time", torch.float32, (T,), dev)
+    num = torch.empty(B, dtype=torch.int32, device=dev)
+    ts = torch.empty(B, dtype=torch.int32, device=dev)
+    ds = torch.empty(B, dtype=torch.int32, device=dev)
+    summ = torch.empty(2, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    _check(lib.sv_schedule_prefix(_ptr(confidence), B, K, _ptr(step_time), T, float(threshold),
+                                  _ptr(num), _ptr(ts), _ptr(ds), _ptr(summ), stream))
+    return ScheduleOutput(num, ts, ds, summ)
 
 
 def sv_read_probe(data: torch.Tensor, groups: int = 2048) -> torch.Tensor:

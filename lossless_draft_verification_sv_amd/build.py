@@ -11,7 +11,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", "sv_kernels.hip"), os.path.join(PKG, "csrc", "sv_probe.hip")]
+SRCS = [os.path.join(PKG, "csrc", n) for n in ("sv_kernels.hip", "sv_probe.hip", "sv_schedule.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsv.so")
 

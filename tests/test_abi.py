@@ -192,3 +192,14 @@ def test_read_probe_rejects_invalid_arguments(lib):
     assert probe(aligned, 12, ctypes.addressof(out), 4, None) == sv.SV_ERR_INVALID_ARG
     assert probe(aligned, 16, ctypes.addressof(out), 0, None) == sv.SV_ERR_INVALID_ARG
     assert "16-byte" in sv.sv_last_error() or "groups" in sv.sv_last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(K=0), dict(K=65), dict(B=4097, K=1),
+                                dict(B=257, K=16), dict(conf=None), dict(num=None),
+                                dict(T=16), dict(table=None, threshold=float("nan"))])
+def test_schedule_rejects_invalid_arguments(lib, kw):
+    args = dict(conf=FAKE, B=4, K=4, table=FAKE, T=4 + 16 + 1, threshold=0.5, num=FAKE,
+                ts=None, ds=None, summary=None, stream=None)
+    args.update(kw)
+    assert lib.sv_schedule_prefix(*args.values()) == sv.SV_ERR_INVALID_ARG
+    assert sv.sv_last_error() != ""

@@ -292,3 +292,20 @@ def flatten(inp: Inputs, order: Optional[Sequence[int]] = None) -> FlatInputs:
             draft[ds[b]:ds[b] + ks[b]] = inp.draft[b, :ks[b]]
     return FlatInputs(w, target, draft, ts, ds, ks, taus, inp.tokens, inp.uniforms,
                       inp.residual)
+
+
+def schedule_confidences(B: int, K: int, seed: int = 1007) -> np.ndarray:
+    """Synthetic per-position draft confidences [B, K] float32 for the prefix scheduler: request
+    b draws from default_rng(SeedSequence([seed, b])) one difficulty level and then a Beta
+    sample per position around it, falling with the position (the pages' per-position
+    acceptance of about 0.9 at the first draft that later positions lower), with occasional
+    exact 1s (confident runs)."""
+    out = np.empty((B, K), dtype=np.float32)
+    for b in range(B):
+        rng = np.random.default_rng(np.random.SeedSequence([seed, b]))
+        level = rng.uniform(0.55, 0.97)
+        mean = np.clip(level - 0.02 * np.arange(K), 0.05, 0.99)
+        c = rng.beta(20.0 * mean, 20.0 * (1.0 - mean)).astype(np.float32)
+        c[rng.random(K) < 0.03] = 1.0
+        out[b] = c
+    return out
