@@ -1,0 +1,139 @@
+"""Pins of the Markov-head oracle (CPU only).
+
+Checked against the pages' worked example (tests/golden/markov/of_course.json), closed forms
+(zero factors leave the base logits; rank-1 factors give a_prev * b_v), a brute-force double
+loop for the bias, and the anchor rule. Planted mistakes must be caught.
+"""
+import json
+import os
+import sys
+import types
+
+import numpy as np
+import pytest
+
+import oracle.markov_oracle as real
+from workloads import to_bf16_bits
+
+M = real
+HERE = os.path.dirname(__file__)
+
+
+def bits(x):
+    return to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def check_golden():
+    g = json.load(open(os.path.join(HERE, "golden", "markov", "of_course.json")))
+    base = np.asarray(g["base_logits"], np.float32)
+    L, R = bits(g["left_factor"]), bits(g["right_factor"])
+    t, c, gaps = M.markov_draft_request(base, "f32", L, R, g["anchor"])
+    assert t.tolist() == g["expected"]["tokens"]
+    assert np.allclose(c, g["expected"]["corrected_logits"])
+    z = np.zeros_like(np.asarray(g["left_factor"]), dtype=np.float32)
+    t0, _, _ = M.markov_draft_request(base, "f32", bits(z), bits(z), g["anchor"])
+    assert t0.tolist() == g["expected"]["tokens_without_head"]
+
+
+def check_closed_forms():
+    rng = np.random.default_rng(3)
+    K, V, R = 4, 37, 8
+    base = rng.normal(0, 2, size=(K, V)).astype(np.float32)
+    zero = bits(np.zeros((V, R)))
+    t, c, _ = M.markov_draft_request(base, "f32", zero, zero, 5)
+    assert np.array_equal(c, base.astype(np.float64))
+    assert t.tolist() == [int(np.argmax(base[k])) for k in range(K)]
+    # rank 1: bias_k[v] = a[prev] * b[v]
+    a = np.round(rng.normal(0, 1, V), 2).astype(np.float32)
+    bv = np.round(rng.normal(0, 1, V), 2).astype(np.float32)
+    La, Rb = bits(a[:, None]), bits(bv[:, None])
+    a64 = M.bf16_factor(La)[:, 0]
+    b64 = M.bf16_factor(Rb)[:, 0]
+    t, c, _ = M.markov_draft_request(base, "f32", La, Rb, 7)
+    prev = 7
+    for k in range(K):
+        want = base[k].astype(np.float64) + a64[prev] * b64
+        assert np.allclose(c[k], want, rtol=0, atol=1e-12)
+        assert t[k] == int(np.argmax(want))
+        prev = t[k]
+
+
+def check_bruteforce_bias():
+    rng = np.random.default_rng(4)
+    K, V, R = 3, 11, 5
+    base = to_bf16_bits(rng.normal(0, 1, size=(K, V)).astype(np.float32))
+    L = bits(rng.normal(0, 1, size=(V, R)))
+    Rf = bits(rng.normal(0, 1, size=(V, R)))
+    t, c, _ = M.markov_draft_request(base, "bf16", L, Rf, 2)
+    Ld, Rd = M.bf16_factor(L), M.bf16_factor(Rf)
+    prev = 2
+    for k in range(K):
+        for v in range(V):
+            s = 0.0
+            for j in range(R):
+                s += Ld[prev, j] * Rd[v, j]
+            want = float(M.decode_logits(base[k], "bf16")[v]) + s
+            assert abs(c[k, v] - want) <= 1e-12
+        prev = int(t[k])
+
+
+def check_anchor_rule():
+    rng = np.random.default_rng(5)
+    K, V, R = 2, 9, 3
+    base = rng.normal(0, 1, size=(K, V)).astype(np.float32)
+    L = bits(rng.normal(0, 3, size=(V, R)))
+    Rf = bits(rng.normal(0, 3, size=(V, R)))
+    _, c_none, _ = M.markov_draft_request(base, "f32", L, Rf, -1)
+    _, c_out, _ = M.markov_draft_request(base, "f32", L, Rf, V)
+    assert np.array_equal(c_none[0], base[0].astype(np.float64))
+    assert np.array_equal(c_out[0], c_none[0])
+    _, c_4, _ = M.markov_draft_request(base, "f32", L, Rf, 4)
+    want = base[0].astype(np.float64) + M.bf16_factor(Rf) @ M.bf16_factor(L)[4]
+    assert np.allclose(c_4[0], want)
+
+
+def check_ties_lowest_index():
+    base = np.array([[1.0, 3.0, 3.0, 0.0]], np.float32)
+    z = bits(np.zeros((4, 2)))
+    t, _, gaps = M.markov_draft_request(base, "f32", z, z, -1)
+    assert t.tolist() == [1] and gaps[0] == 0.0
+    _, _, amb = M.markov_draft(base[None], "f32", z, z)
+    assert amb[0]
+
+
+CHECKS = [check_golden, check_closed_forms, check_bruteforce_bias, check_anchor_rule,
+          check_ties_lowest_index]
+
+
+@pytest.mark.parametrize("chk", CHECKS, ids=lambda f: f.__name__)
+def test_markov_oracle_pins(chk):
+    chk()
+
+
+SRC = open(real.__file__).read()
+MUTATIONS = {
+    "factors_swapped": ("z = z + Rf @ L[prev]", "z = z + L @ Rf[prev]"),
+    "bias_from_own_position": ("        prev = y\n", "        prev = prev\n"),
+    "no_anchor_bias": ("    prev = int(anchor)\n", "    prev = -1\n"),
+    "bias_sign_flipped": ("z = z + Rf @ L[prev]", "z = z - Rf @ L[prev]"),
+    "ties_highest_index": ("y = argmax_lowest(z)", "y = int(len(z) - 1 - np.argmax(z[::-1]))"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    old, new = MUTATIONS[name]
+    assert SRC.count(old) == 1, name
+    mod = types.ModuleType(f"oracle.markov_mutant_{name}")
+    mod.__package__ = "oracle"
+    monkeypatch.setitem(sys.modules, mod.__name__, mod)
+    exec(compile(SRC.replace(old, new), f"<mutant {name}>", "exec"), mod.__dict__)
+    monkeypatch.setattr(sys.modules[__name__], "M", mod)
+    caught = False
+    for chk in CHECKS:
+        try:
+            chk()
+        except Exception:
+            caught = True
+            break
+    assert caught, name
