@@ -183,6 +183,33 @@ int sv_schedule_prefix(const float* confidence, int B, int K, const float* step_
                        float threshold, int32_t* num_draft, int32_t* target_row_start,
                        int32_t* draft_row_start, float* summary, void* stream);
 
+/* Markov-head correction of a parallel draft block ("Accelerating Large-Model Inference ...",
+ * section 3, Markov Head; DSpark paper review 4.1): left to right over positions k = 0..K-1,
+ *   corrected[b][k][v] = base[b][k][v] + sum_j L[prev][j] * Rf[v][j],
+ *   prev = anchor[b] for k = 0 (no bias when anchor is NULL or outside [0, V)), else the token
+ *   chosen at k-1;  token[b][k] = argmax_v corrected[b][k][v] (lowest index on ties).
+ * The bias is a dense contraction over the rank on the matrix cores (bf16 factors, fp32
+ * accumulation); the corrected logits are the block's draft logits for verification.
+ *
+ *  base_logits   [B, K, V] dtype (SV_DTYPE_F32 / SV_DTYPE_BF16), device
+ *  left_factor   [V, R] bf16 bits (uint16), device, 16-byte aligned: row = previous token
+ *  right_factor  [V, R] bf16 bits, device, 16-byte aligned: row = candidate token
+ *  R             rank, a multiple of 16 in [16, 1024] (256 in the pages)
+ *  anchor        [B] int32 device or NULL
+ *  draft_tokens  [B, K] int32 out; draft_logits [B, K, V] dtype out or NULL (bf16 rounds to
+ *                nearest even)
+ *  workspace     sv_markov_workspace_bytes(B, V) bytes, 256-byte aligned, device, owned by the
+ *                caller, no clearing needed. It is left holding per-tile argmaxes, not tagged
+ *                words: zero it before handing the same memory to sv_verify_*.
+ * 2K launches on `stream`. Returns SV_OK, SV_ERR_INVALID_ARG, SV_ERR_WORKSPACE,
+ * SV_ERR_UNSUPPORTED or SV_ERR_HIP; nothing is launched unless SV_OK.
+ */
+size_t sv_markov_workspace_bytes(int B, int V);
+int sv_markov_draft(const void* base_logits, int dtype, int B, int K, int V,
+                    const uint16_t* left_factor, const uint16_t* right_factor, int R,
+                    const int32_t* anchor, int32_t* draft_tokens, void* draft_logits,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Read probe (a measurement aid, not a step of the method): the plainest stream over a device
  * buffer, so that the row stream can be compared with the read bandwidth this device reaches.
  * `groups` work-groups of 256 threads read every 16-byte word of data[0, bytes) once with

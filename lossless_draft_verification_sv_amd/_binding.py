@@ -64,6 +64,11 @@ def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
         lib.sv_verify_ragged.restype = i32
         lib.sv_schedule_prefix.argtypes = [vp, i32, i32, vp, i32, f32, vp, vp, vp, vp, vp]
         lib.sv_schedule_prefix.restype = i32
+        lib.sv_markov_workspace_bytes.argtypes = [i32, i32]
+        lib.sv_markov_workspace_bytes.restype = sz
+        lib.sv_markov_draft.argtypes = [vp, i32, i32, i32, i32, vp, vp, i32, vp, vp, vp, vp, sz,
+                                        vp]
+        lib.sv_markov_draft.restype = i32
         lib.sv_read_probe.argtypes = [vp, sz, vp, i32, vp]
         lib.sv_read_probe.restype = i32
         _lib = lib
@@ -115,10 +120,12 @@ def _need(t: torch.Tensor, name: str, dtype, shape, device) -> None:
 _ws_cache = {}
 
 
-def _workspace(device: torch.device, stream: int, nbytes: int) -> torch.Tensor:
-    """One cached workspace per (device, stream), zero-filled when allocated: calls on one
-    stream never overlap, and a workspace needs no clearing between calls."""
-    key = (device, stream)
+def _workspace(device: torch.device, stream: int, nbytes: int,
+               kind: str = "verify") -> torch.Tensor:
+    """One cached workspace per (device, stream, kind), zero-filled when allocated: calls on one
+    stream never overlap, and a workspace needs no clearing between calls. The Markov head's
+    workspace is a separate kind: the words it leaves behind carry no call tag."""
+    key = (device, stream, kind)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -283,6 +290,38 @@ def sv_schedule_prefix(confidence: torch.Tensor, step_time: Optional[torch.Tenso
     _check(lib.sv_schedule_prefix(_ptr(confidence), B, K, _ptr(step_time), T, float(threshold),
                                   _ptr(num), _ptr(ts), _ptr(ds), _ptr(summ), stream))
     return ScheduleOutput(num, ts, ds, summ)
+
+
+def sv_markov_draft(base: torch.Tensor, left_factor: torch.Tensor, right_factor: torch.Tensor,
+                    anchor: Optional[torch.Tensor] = None, return_logits: bool = True):
+    """Markov-head correction of a draft block on the tensors' GPU (see sv_markov_draft in
+    include/sv.h). base [B, K, V] float32 or bfloat16; left_factor, right_factor [V, R]
+    bfloat16; anchor [B] int32 or None. Returns (tokens [B, K] int32, corrected logits
+    [B, K, V] of base's dtype or None)."""
+    lib = load_library()
+    if base.dim() != 3:
+        raise ValueError("base must be [B, K, V]")
+    B, K, V = base.shape
+    dev = base.device
+    if dev.type != "cuda":
+        raise ValueError("base must be a GPU tensor")
+    _need(base, "base", base.dtype, (B, K, V), dev)
+    if left_factor.dim() != 2:
+        raise ValueError("left_factor must be [V, R]")
+    R = left_factor.shape[1]
+    _need(left_factor, "left_factor", torch.bfloat16, (V, R), dev)
+    _need(right_factor, "right_factor", torch.bfloat16, (V, R), dev)
+    if anchor is not None:
+        _need(anchor, "anchor", torch.int32, (B,), dev)
+    tokens = torch.empty(B, K, dtype=torch.int32, device=dev)
+    out = torch.empty_like(base) if return_logits else None
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    nbytes = int(lib.sv_markov_workspace_bytes(B, V))
+    ws = _workspace(dev, stream, nbytes, "markov")
+    _check(lib.sv_markov_draft(_ptr(base), _dtype_code(base), B, K, V, _ptr(left_factor),
+                               _ptr(right_factor), R, _ptr(anchor), _ptr(tokens), _ptr(out),
+                               _ptr(ws), ws.numel(), stream))
+    return tokens, out
 
 
 def sv_read_probe(data: torch.Tensor, groups: int = 2048) -> torch.Tensor:

@@ -11,7 +11,8 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", n) for n in ("sv_kernels.hip", "sv_probe.hip", "sv_schedule.hip")]
+SRCS = [os.path.join(PKG, "csrc", n) for n in ("sv_kernels.hip", "sv_probe.hip", "sv_schedule.hip",
+                                                "sv_markov.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsv.so")
 

@@ -1,0 +1,574 @@
+// Markov-head correction of a parallel draft block (declared in sv.h): left to right over the K
+// positions, position k's base logits get the low-rank bias of the token chosen at k-1 (the
+// anchor at k = 0), bias[v] = sum_j L[prev][j] * Rf[v][j], and the position's token is the
+// argmax of the corrected logits ("Accelerating Large-Model Inference ...", section 3, Markov
+// Head; the DSpark paper review, 4.1).
+//
+// Per position, two launches:
+//   markov_bias_tile: work-group (vocabulary tile of 128, request block of 64); the bias block
+//     [64 requests x 128 tokens] = L[prev rows] x Rf[tile rows]^T is a dense contraction over
+//     the rank R, done on MFMA (v_mfma_f32_32x32x8_bf16: each wave two 32x32 blocks, bf16 in,
+//     fp32 accumulate). Its epilogue adds the base logits, writes the corrected logits (the
+//     block's draft logits) and the tile's argmax per request (value, index) to the workspace.
+//   markov_finish: one work-group per request reduces the tile argmaxes (lowest index on ties)
+//     to the position's token, which the next position's launch reads as its previous token.
+// The rank index is permuted identically in both operands (each lane reads 16 contiguous bytes
+// of its factor row per pair of MFMA steps); the contraction sums over all of it.
+
+#include <hip/hip_runtime.h>
+
+#include <float.h>
+#include <limits.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "sv.h"
+#include "sv_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kReqBlock = 64;            // requests per work-group: two 32-row MFMA blocks
+constexpr int kTileV = 32 * kWaves;      // vocabulary entries per work-group: 32 per wave
+constexpr int kRankChunk = 256;          // rank indices per pass (one pass at the usual rank)
+constexpr int kPairs = kRankChunk / 16;  // pairs of MFMA steps per pass
+constexpr int kARow = kRankChunk + 8;    // LDS row stride of the staged left rows, in bf16
+constexpr int kMaxRank = 1024;
+constexpr int kFinishLoads = 8;          // partials each finishing thread has in flight
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+struct Logit;
+template <>
+struct Logit<float> {
+  __device__ static float get(float x) { return x; }
+  __device__ static void put(float* p, float x) { *p = x; }
+};
+template <>
+struct Logit<uint16_t> {
+  __device__ static float get(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+  __device__ static void put(uint16_t* p, float x) {  // round to nearest, ties to even
+    const uint32_t b = __float_as_uint(x);
+    *p = (x != x) ? (uint16_t)0x7FC0 : (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+  }
+};
+
+__device__ __forceinline__ short4_t lo4(v4u32 v) {
+  short4_t s;
+  s[0] = (short)(v.x & 0xffff); s[1] = (short)(v.x >> 16);
+  s[2] = (short)(v.y & 0xffff); s[3] = (short)(v.y >> 16);
+  return s;
+}
+__device__ __forceinline__ short4_t hi4(v4u32 v) {
+  short4_t s;
+  s[0] = (short)(v.z & 0xffff); s[1] = (short)(v.z >> 16);
+  s[2] = (short)(v.w & 0xffff); s[3] = (short)(v.w >> 16);
+  return s;
+}
+
+// (value, index) order of the argmax: larger value first, then the lower index.
+__device__ __forceinline__ bool better(float z, int i, float best, int bi) {
+  return z > best || (z == best && i < bi);
+}
+
+// Work-group g of a position covers vocabulary tile g / nrb and request block g % nrb; the
+// launch index is spread so that the work-groups of one XCD (launch index mod 8) take a
+// contiguous range of g, and so the request blocks of a tile share that XCD's L2.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void markov_bias_tile(
+    const T* __restrict__ base, T* __restrict__ out, int B, int K, int V, int k,
+    const uint16_t* __restrict__ left, const uint16_t* __restrict__ right, int R,
+    const int32_t* __restrict__ prev_tok, int prev_stride, uint64_t* __restrict__ part, int ntile,
+    int nrb) {
+  __shared__ union __attribute__((aligned(16))) {
+    uint16_t a[kReqBlock][kARow];        // left-factor rows of the block's previous tokens
+    float z[kReqBlock][kTileV + 1];      // corrected logits, for the tile argmax
+  } sm;
+  const int n = ntile * nrb, per = (n + 7) / 8;
+  const int g = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+  if (g >= n) return;  // uniform over the work-group
+  const int tile = g / nrb, b0 = (g % nrb) * kReqBlock;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, c = lane & 31;
+  const int v = tile * kTileV + wave * 32 + c;  // this lane's column of the B operand
+  const int vr = v < V ? v : V - 1;
+
+  // staging rows of this thread: m = tid / 32 + 8 u, 16-byte word tid % 32 of the rank chunk
+  const int sw = tid & 31;
+  int srow[kReqBlock / 8];
+#pragma unroll
+  for (int u = 0; u < kReqBlock / 8; ++u) {
+    const int b = b0 + (tid >> 5) + 8 * u;
+    const int p = (b < B && prev_tok != nullptr) ? prev_tok[(size_t)b * prev_stride] : -1;
+    srow[u] = (p >= 0 && p < V) ? p : -1;
+  }
+  // base logits of this lane's 32 outputs, loaded ahead of the contraction
+  T bv[2][16];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      int b = b0 + rb * 32 + 8 * (i / 4) + 4 * h + (i % 4);
+      b = b < B ? b : B - 1;
+      bv[rb][i] = base[((size_t)b * K + k) * (size_t)V + vr];
+    }
+
+  float16_t acc[2] = {{}, {}};
+  const v4u32 zero4 = {0u, 0u, 0u, 0u};
+  for (int c0 = 0; c0 < R; c0 += kRankChunk) {
+    const int np = (R - c0) / 16 < kPairs ? (R - c0) / 16 : kPairs;  // pairs in this pass
+    // B operand: rank indices c0 + 16 t + 8 h .. + 7 of factor row vr, all passes in flight
+    const v4u32* rrow = reinterpret_cast<const v4u32*>(right + (size_t)vr * R + c0);
+    v4u32 bq[kPairs];
+#pragma unroll
+    for (int t = 0; t < kPairs; ++t) bq[t] = rrow[2 * (t < np ? t : np - 1) + h];
+    // A operand: stage the block's left rows (zero for no previous token or past the rank)
+    v4u32 aw[kReqBlock / 8];
+#pragma unroll
+    for (int u = 0; u < kReqBlock / 8; ++u) {
+      const int row = srow[u] < 0 ? 0 : srow[u];
+      const int w = 2 * np > sw ? sw : 2 * np - 1;
+      aw[u] = reinterpret_cast<const v4u32*>(left + (size_t)row * R + c0)[w];
+    }
+    if (c0 > 0) __syncthreads();  // the previous pass has read the staged rows
+#pragma unroll
+    for (int u = 0; u < kReqBlock / 8; ++u) {
+      const bool ok = srow[u] >= 0 && sw < 2 * np;
+      *reinterpret_cast<v4u32*>(&sm.a[(tid >> 5) + 8 * u][8 * sw]) = ok ? aw[u] : zero4;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < kPairs; ++t) {
+      const v4u32 b = t < np ? bq[t] : zero4;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const v4u32 a = *reinterpret_cast<const v4u32*>(&sm.a[rb * 32 + c][16 * t + 8 * h]);
+        acc[rb] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(lo4(a), lo4(b), acc[rb], 0, 0, 0);
+        acc[rb] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(hi4(a), hi4(b), acc[rb], 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();  // every wave is done with the staged rows before they become sm.z
+  // epilogue: register i of lane (h, c) holds row 8*(i/4) + 4*h + i%4 of the 32x32 block
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = rb * 32 + 8 * (i / 4) + 4 * h + (i % 4);
+      const int b = b0 + m;
+      const bool ok = b < B && v < V;
+      const float z = ok ? Logit<T>::get(bv[rb][i]) + acc[rb][i] : -INFINITY;
+      if (ok && out != nullptr) Logit<T>::put(out + ((size_t)b * K + k) * (size_t)V + v, z);
+      sm.z[m][wave * 32 + c] = z;
+    }
+  }
+  __syncthreads();
+  // tile argmax per request: 4 threads per row, 32 columns each, ascending index
+  const int m = tid >> 2, q = tid & 3;
+  float best = -INFINITY;
+  int bi = INT_MAX;
+  for (int j = 0; j < 32; ++j) {
+    const int col = q * 32 + j;
+    const float z = sm.z[m][col];
+    if (z > best) {
+      best = z;
+      bi = tile * kTileV + col;
+    }
+  }
+#pragma unroll
+  for (int s = 1; s <= 2; s <<= 1) {
+    const float b2 = __shfl_xor(best, s);
+    const int i2 = __shfl_xor(bi, s);
+    if (better(b2, i2, best, bi)) {
+      best = b2;
+      bi = i2;
+    }
+  }
+  const int b = b0 + m;
+  if (q == 0 && b < B)
+    part[(size_t)b * ntile + tile] = ((uint64_t)__float_as_uint(best) << 32) | (uint32_t)bi;
+}
+
+// Ranks up to kRankChunk: a persistent form of the same step. Work-group w walks a contiguous
+// range of items (request block, vocabulary tile of kStreamTile), request block slowest. The
+// left rows of the request block stay in LDS while the tiles stream through; the factor rows of
+// the next item are loaded while the current one is contracted and finished. Each wave owns 16
+// columns (v_mfma_f32_16x16x32_bf16: one step per 32 rank indices and 16x16 block, four blocks
+// for the 64 requests), so a lane holds its share of a factor row in R/8 registers and two
+// items' worth fit beside the accumulators. The epilogue goes through LDS so that base and
+// corrected logits move as 16-byte vectors along each request's row.
+constexpr int kStreamTile = 16 * kWaves;     // vocabulary entries per item
+constexpr int kSteps = kRankChunk / 32;      // MFMA steps per item at the largest rank
+constexpr int kZRow = kStreamTile + 4;       // LDS row stride of the corrected tile, in floats
+
+template <typename T>
+struct Base {
+  static constexpr int kVec = 16 / (int)sizeof(T);  // logits per 16-byte vector
+  static constexpr int kWords = 16 / kVec;          // vectors of the 16 logits a thread finishes
+  v4u32 w[kWords];
+};
+
+// Logit e (0..15) of a thread's finishing set, from its raw 16-byte vectors.
+template <typename T>
+__device__ __forceinline__ float logit_at(const Base<T>& bv, int e) {
+  constexpr int kVec = Base<T>::kVec, kPer32 = 4 / (int)sizeof(T);  // logits per 32-bit word
+  const uint32_t word = bv.w[e / kVec][(e % kVec) / kPer32];
+  if constexpr (sizeof(T) == 4) return __uint_as_float(word);
+  else return __uint_as_float((e & 1) ? (word & 0xffff0000u) : (word << 16));
+}
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// Factor row words of this lane's column of the tile (lane % 16): rank indices
+// 32 s + 8 (lane / 16) .. + 7 for step s, 16-byte word 4 s + lane / 16 of the row. Words past
+// the row (R not a multiple of 32, or steps past ns) re-read its last word; the contraction
+// zeroes them.
+__device__ __forceinline__ void load_factor(v4u32 (&bq)[kSteps], const uint16_t* __restrict__ right,
+                                            int V, int R, int tile) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = R / 8;
+  const int v = tile * kStreamTile + wave * 16 + (lane & 15);
+  const v4u32* rrow = reinterpret_cast<const v4u32*>(right + (size_t)(v < V ? v : V - 1) * R);
+#pragma unroll
+  for (int t = 0; t < kSteps; ++t) {
+    const int wi = 4 * t + (lane >> 4);
+    bq[t] = rrow[wi < nw ? wi : nw - 1];
+  }
+}
+
+// Base logits that thread (m, q) finishes: row m of the block, columns 16 q .. 16 q + 15 of the
+// tile, clamped into the batch and the vocabulary (the epilogue masks them). VEC: rows are
+// 16-byte aligned and V is a multiple of the vector, so a vector starting inside the row lies
+// inside it; otherwise element by element.
+template <typename T, bool VEC>
+__device__ __forceinline__ void load_base(Base<T>& bv, const T* __restrict__ base, int B, int K,
+                                          int V, int k, int tile, int b0) {
+  constexpr int kVec = Base<T>::kVec;
+  const int tid = threadIdx.x;
+  int b = b0 + (tid >> 2);
+  b = b < B ? b : B - 1;
+  const T* row = base + ((size_t)b * K + k) * (size_t)V;
+#pragma unroll
+  for (int w = 0; w < Base<T>::kWords; ++w) {
+    const int v0 = tile * kStreamTile + 16 * (tid & 3) + w * kVec;
+    if constexpr (VEC) {
+      bv.w[w] = *reinterpret_cast<const v4u32*>(row + (v0 < V ? v0 : V - kVec));
+    } else {
+      uint32_t e[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        if constexpr (sizeof(T) == 4) {
+          e[x] = __float_as_uint(row[v0 + x < V ? v0 + x : V - 1]);
+        } else {
+          const int v1 = v0 + 2 * x < V ? v0 + 2 * x : V - 1;
+          const int v2 = v0 + 2 * x + 1 < V ? v0 + 2 * x + 1 : V - 1;
+          e[x] = (uint32_t)row[v1] | ((uint32_t)row[v2] << 16);
+        }
+      }
+      bv.w[w] = v4u32{e[0], e[1], e[2], e[3]};
+    }
+  }
+}
+
+// Previous tokens of the rows this thread stages (rows tid / 32 + 8 u of the request block at
+// b0); -1 where there is none (past B, no previous tokens, or outside [0, V)).
+__device__ __forceinline__ void stage_tokens(int (&p)[kReqBlock / 8],
+                                             const int32_t* __restrict__ prev_tok,
+                                             int prev_stride, int B, int V, int b0) {
+#pragma unroll
+  for (int u = 0; u < kReqBlock / 8; ++u) {
+    const int b = b0 + ((int)threadIdx.x >> 5) + 8 * u;
+    const int x = (b < B && prev_tok != nullptr) ? prev_tok[(size_t)b * prev_stride] : -1;
+    p[u] = (x >= 0 && x < V) ? x : -1;
+  }
+}
+
+// Stages the left-factor rows of the block's previous tokens into sa (rank words past R and
+// rows without a token are zero), then waits for the whole work-group.
+__device__ __forceinline__ void stage_rows(uint16_t (*sa)[kARow], const int (&p)[kReqBlock / 8],
+                                           const uint16_t* __restrict__ left, int R) {
+  const int sw = threadIdx.x & 31, nw = R / 8;  // 16-byte words per row
+  const int wd = sw < nw ? sw : nw - 1;
+  v4u32 aw[kReqBlock / 8];
+#pragma unroll
+  for (int u = 0; u < kReqBlock / 8; ++u)
+    aw[u] = reinterpret_cast<const v4u32*>(left + (size_t)(p[u] >= 0 ? p[u] : 0) * R)[wd];
+#pragma unroll
+  for (int u = 0; u < kReqBlock / 8; ++u) {
+    const bool ok = p[u] >= 0 && sw < nw;
+    *reinterpret_cast<v4u32*>(&sa[(threadIdx.x >> 5) + 8 * u][8 * sw]) =
+        ok ? aw[u] : v4u32{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+}
+
+struct StreamArgs {
+  int B, K, V, k, R, ns, ntile, prev_stride;
+  const uint16_t* left;
+  const uint16_t* right;
+  const int32_t* prev_tok;
+  uint64_t* part;
+};
+
+// One item of the staged request block: contract with the factor words in cur (the next
+// item's are requested into nxt first), add the base logits, write the corrected logits and the
+// tile argmax of every request of the block.
+template <typename T, bool VEC>
+__device__ __forceinline__ void stream_item(const StreamArgs& a, const T* __restrict__ base,
+                                            T* __restrict__ out, uint16_t (*sa)[kARow],
+                                            float (*sz)[kZRow], int j, int jend,
+                                            const v4u32 (&cur)[kSteps], v4u32 (&nxt)[kSteps]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tile = j % a.ntile, b0 = (j / a.ntile) * kReqBlock;
+  Base<T> bv;
+  load_base<T, VEC>(bv, base, a.B, a.K, a.V, a.k, tile, b0);
+  // unconditional (the last item re-reads its own tile) so that the waits below stay exact
+  load_factor(nxt, a.right, a.V, a.R, (j + 1 < jend ? j + 1 : j) % a.ntile);
+  float4_t acc[4] = {{}, {}, {}, {}};
+#pragma unroll
+  for (int t = 0; t < kSteps; ++t) {
+    if (t < a.ns) {  // uniform
+      const bool inside = 4 * t + (lane >> 4) < a.R / 8;
+      const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, inside ? cur[t] : v4u32{0u, 0u, 0u, 0u});
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const v4u32 x =
+            *reinterpret_cast<const v4u32*>(&sa[rb * 16 + (lane & 15)][32 * t + 8 * (lane >> 4)]);
+        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x), bfr,
+                                                          acc[rb], 0, 0, 0);
+      }
+    }
+  }
+  // register i of lane l holds row 4 (l / 16) + i, column l % 16 of the 16x16 block
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      sz[rb * 16 + 4 * (lane >> 4) + i][wave * 16 + (lane & 15)] = acc[rb][i];
+  __syncthreads();
+  // thread (m, q): row m of the block, columns 16 q .. 16 q + 15, ascending
+  const int m = tid >> 2, q = tid & 3, b = b0 + m;
+  const int v0 = tile * kStreamTile + 16 * q;
+  float z[16];
+  float best = -INFINITY;
+  int bi = INT_MAX;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const bool ok = b < a.B && v0 + e < a.V;
+    z[e] = ok ? logit_at<T>(bv, e) + sz[m][16 * q + e] : -INFINITY;
+    if (z[e] > best) {
+      best = z[e];
+      bi = v0 + e;
+    }
+  }
+  if (out != nullptr && b < a.B) {
+    T* orow = out + ((size_t)b * a.K + a.k) * (size_t)a.V + v0;
+    if constexpr (VEC) {  // whole vectors: the row ends on a vector boundary
+      constexpr int kVec = Base<T>::kVec;
+#pragma unroll
+      for (int w = 0; w < Base<T>::kWords; ++w) {
+        if (v0 + w * kVec < a.V) {
+          if constexpr (sizeof(T) == 4) {
+            *reinterpret_cast<float4*>(orow + 4 * w) =
+                make_float4(z[4 * w], z[4 * w + 1], z[4 * w + 2], z[4 * w + 3]);
+          } else {
+            uint16_t r[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) Logit<T>::put(&r[e], z[8 * w + e]);
+            *reinterpret_cast<v4u32*>(orow + 8 * w) =
+                v4u32{r[0] | ((uint32_t)r[1] << 16), r[2] | ((uint32_t)r[3] << 16),
+                      r[4] | ((uint32_t)r[5] << 16), r[6] | ((uint32_t)r[7] << 16)};
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (v0 + e < a.V) Logit<T>::put(orow + e, z[e]);
+    }
+  }
+#pragma unroll
+  for (int s = 1; s <= 2; s <<= 1) {
+    const float b2 = __shfl_xor(best, s);
+    const int i2 = __shfl_xor(bi, s);
+    if (better(b2, i2, best, bi)) {
+      best = b2;
+      bi = i2;
+    }
+  }
+  if (q == 0 && b < a.B)
+    a.part[(size_t)b * a.ntile + tile] = ((uint64_t)__float_as_uint(best) << 32) | (uint32_t)bi;
+  __syncthreads();  // sz is rewritten by the next item
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void markov_stream(const T* __restrict__ base,
+                                                          T* __restrict__ out, StreamArgs a,
+                                                          int nrb, int per_group) {
+  __shared__ __attribute__((aligned(16))) uint16_t sa[kReqBlock][kARow];
+  __shared__ __attribute__((aligned(16))) float sz[kReqBlock][kZRow];
+  const int n = a.ntile * nrb, lanes8 = (int)gridDim.x / 8;
+  const int w = (int)(blockIdx.x & 7) * lanes8 + (int)(blockIdx.x >> 3);
+  const int j0 = w * per_group, j1 = j0 + per_group < n ? j0 + per_group : n;
+  if (j0 >= j1) return;  // uniform over the work-group
+  v4u32 f0[kSteps], f1[kSteps];
+  for (int j = j0; j < j1;) {  // runs of items that share a request block
+    const int rbk = j / a.ntile;
+    const int jend = (rbk + 1) * a.ntile < j1 ? (rbk + 1) * a.ntile : j1;
+    {  // previous tokens first, then the first item's factor words, then the left rows
+      int p[kReqBlock / 8];
+      stage_tokens(p, a.prev_tok, a.prev_stride, a.B, a.V, rbk * kReqBlock);
+      load_factor(f0, a.right, a.V, a.R, j % a.ntile);
+      if (j > j0) __syncthreads();  // the previous block's rows are no longer read
+      stage_rows(sa, p, a.left, a.R);
+    }
+    for (; j < jend; j += 2) {  // two items per trip, the factor buffers alternating
+      stream_item<T, VEC>(a, base, out, sa, sz, j, jend, f0, f1);
+      if (j + 1 < jend) stream_item<T, VEC>(a, base, out, sa, sz, j + 1, jend, f1, f0);
+    }
+  }
+}
+
+// One work-group per request: the argmax over the tile partials (lowest index on ties) is the
+// position's token. A request whose logits are all -inf or NaN gets token 0.
+__global__ __launch_bounds__(kThreads) void markov_finish(const uint64_t* __restrict__ part,
+                                                          int ntile, int K, int k,
+                                                          int32_t* __restrict__ tokens) {
+  const int b = blockIdx.x;
+  const uint64_t* row = part + (size_t)b * ntile;
+  float best = -INFINITY;
+  int bi = INT_MAX;
+  for (int t0 = 0; t0 < ntile; t0 += kThreads * kFinishLoads) {
+    uint64_t w[kFinishLoads];
+#pragma unroll
+    for (int u = 0; u < kFinishLoads; ++u) {
+      const int t = t0 + u * kThreads + (int)threadIdx.x;
+      w[u] = row[t < ntile ? t : ntile - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < kFinishLoads; ++u) {
+      const float z = __uint_as_float((uint32_t)(w[u] >> 32));
+      const int i = (int)(uint32_t)w[u];
+      if (better(z, i, best, bi)) {  // a repeated last partial changes nothing
+        best = z;
+        bi = i;
+      }
+    }
+  }
+  for (int s = 32; s >= 1; s >>= 1) {
+    const float b2 = __shfl_xor(best, s);
+    const int i2 = __shfl_xor(bi, s);
+    if (better(b2, i2, best, bi)) {
+      best = b2;
+      bi = i2;
+    }
+  }
+  __shared__ float sb[kWaves];
+  __shared__ int si[kWaves];
+  if ((threadIdx.x & 63) == 0) {
+    sb[threadIdx.x >> 6] = best;
+    si[threadIdx.x >> 6] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kWaves; ++w)
+      if (better(sb[w], si[w], best, bi)) {
+        best = sb[w];
+        bi = si[w];
+      }
+    tokens[(size_t)b * K + k] = bi == INT_MAX ? 0 : bi;
+  }
+}
+
+bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <typename T>
+int launch_all(const void* base, void* out, int B, int K, int V, const uint16_t* left,
+               const uint16_t* right, int R, const int32_t* anchor, int32_t* tokens,
+               uint64_t* part, hipStream_t s) {
+  const int nrb = (B + kReqBlock - 1) / kReqBlock;
+  const bool stream = R <= kRankChunk;
+  const int ntile = stream ? (V + kStreamTile - 1) / kStreamTile : (V + kTileV - 1) / kTileV;
+  const int n = ntile * nrb;
+  const int groups = 8 * ((n + 7) / 8);
+  // persistent form: up to three work-groups per CU, each a contiguous run of equally many items
+  const int slots = 3 * cu_count();
+  const int per = (n + slots - 1) / slots;
+  const int pgroups = 8 * (((n + per - 1) / per + 7) / 8);
+  const bool vec_rows = aligned16(base) && aligned16(out) && ((size_t)V * sizeof(T)) % 16 == 0;
+  for (int k = 0; k < K; ++k) {
+    const int32_t* prev = k == 0 ? anchor : tokens + (k - 1);
+    const int stride = k == 0 ? 1 : K;
+    if (stream) {
+      const StreamArgs a{B, K, V, k, R, (R + 31) / 32, ntile, stride, left, right, prev, part};
+      if (vec_rows)
+        hipLaunchKernelGGL((markov_stream<T, true>), dim3(pgroups), dim3(kThreads), 0, s,
+                           static_cast<const T*>(base), static_cast<T*>(out), a, nrb, per);
+      else
+        hipLaunchKernelGGL((markov_stream<T, false>), dim3(pgroups), dim3(kThreads), 0, s,
+                           static_cast<const T*>(base), static_cast<T*>(out), a, nrb, per);
+    } else {
+      hipLaunchKernelGGL(markov_bias_tile<T>, dim3(groups), dim3(kThreads), 0, s,
+                         static_cast<const T*>(base), static_cast<T*>(out), B, K, V, k, left,
+                         right, R, prev, stride, part, ntile, nrb);
+    }
+    hipLaunchKernelGGL(markov_finish, dim3(B), dim3(kThreads), 0, s, part, ntile, K, k, tokens);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return sv_internal_fail(SV_ERR_HIP, hipGetErrorString(e));
+  return SV_OK;
+}
+
+}  // namespace
+
+extern "C" size_t sv_markov_workspace_bytes(int B, int V) {
+  if (B < 1 || V < 1) return 0;
+  return (size_t)B * ((V + kStreamTile - 1) / kStreamTile) * 8;  // tile partials, either form
+}
+
+extern "C" int sv_markov_draft(const void* base_logits, int dtype, int B, int K, int V,
+                               const uint16_t* left_factor, const uint16_t* right_factor, int R,
+                               const int32_t* anchor, int32_t* draft_tokens, void* draft_logits,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  sv_internal_clear_error();
+  if (B < 1 || B > (1 << 20) || K < 1 || K > 64 || V < 1 || V > (1 << 26))
+    return sv_internal_fail(SV_ERR_INVALID_ARG, "need 1 <= B <= 2^20, 1 <= K <= 64, 1 <= V <= 2^26");
+  if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16)
+    return sv_internal_fail(SV_ERR_INVALID_ARG, "dtype must be SV_DTYPE_F32 or SV_DTYPE_BF16");
+  if (R < 16 || R > kMaxRank || R % 16 != 0)
+    return sv_internal_fail(SV_ERR_INVALID_ARG, "rank R must be a multiple of 16 in [16, 1024]");
+  if (!base_logits || !left_factor || !right_factor || !draft_tokens)
+    return sv_internal_fail(SV_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (reinterpret_cast<uintptr_t>(left_factor) % 16 || reinterpret_cast<uintptr_t>(right_factor) % 16)
+    return sv_internal_fail(SV_ERR_INVALID_ARG, "factors must be 16-byte aligned");
+  const size_t need = sv_markov_workspace_bytes(B, V);
+  if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256)
+    return sv_internal_fail(SV_ERR_WORKSPACE, "workspace missing, too small or not 256-byte aligned");
+  if ((long)((V + kStreamTile - 1) / kStreamTile) * ((B + kReqBlock - 1) / kReqBlock) >= (1L << 30))
+    return sv_internal_fail(SV_ERR_UNSUPPORTED, "grid too large");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint64_t* part = static_cast<uint64_t*>(workspace);
+  if (dtype == SV_DTYPE_F32)
+    return launch_all<float>(base_logits, draft_logits, B, K, V, left_factor, right_factor, R,
+                             anchor, draft_tokens, part, s);
+  return launch_all<uint16_t>(base_logits, draft_logits, B, K, V, left_factor, right_factor, R,
+                              anchor, draft_tokens, part, s);
+}

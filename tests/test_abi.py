@@ -203,3 +203,21 @@ def test_schedule_rejects_invalid_arguments(lib, kw):
     args.update(kw)
     assert lib.sv_schedule_prefix(*args.values()) == sv.SV_ERR_INVALID_ARG
     assert sv.sv_last_error() != ""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), sv.SV_ERR_INVALID_ARG), (dict(K=65), sv.SV_ERR_INVALID_ARG),
+    (dict(V=0), sv.SV_ERR_INVALID_ARG), (dict(dtype=9), sv.SV_ERR_INVALID_ARG),
+    (dict(R=8), sv.SV_ERR_INVALID_ARG), (dict(R=264), sv.SV_ERR_INVALID_ARG),
+    (dict(R=2048), sv.SV_ERR_INVALID_ARG), (dict(base=None), sv.SV_ERR_INVALID_ARG),
+    (dict(left=None), sv.SV_ERR_INVALID_ARG), (dict(tokens=None), sv.SV_ERR_INVALID_ARG),
+    (dict(left=FAKE + 8), sv.SV_ERR_INVALID_ARG), (dict(ws=None), sv.SV_ERR_WORKSPACE),
+    (dict(ws_bytes=8), sv.SV_ERR_WORKSPACE), (dict(ws=WS + 16), sv.SV_ERR_WORKSPACE),
+])
+def test_markov_rejects_invalid_arguments(lib, kw, status):
+    args = dict(base=FAKE, dtype=sv.SV_DTYPE_BF16, B=4, K=4, V=1000, left=FAKE, right=FAKE,
+                R=256, anchor=None, tokens=FAKE, logits=None, ws=WS, ws_bytes=1 << 30,
+                stream=None)
+    args.update(kw)
+    assert lib.sv_markov_draft(*args.values()) == status
+    assert sv.sv_last_error() != ""

@@ -1,0 +1,173 @@
+"""Markov-head correction of a draft block on the GPU against the Markov oracle.
+
+Parity bar: draft tokens bit-exact at every position whose oracle top-2 gap is at least
+AMBIGUOUS_GAP and whose earlier tokens agree (a float32 sum of R bf16 products may order two
+logits closer than that the other way; after such a position the chains may part). Corrected
+logits, wherever the earlier tokens agree: float32 output within 2e-5 + 1e-6 |z| of the fp64
+value (R products of bf16 factors are exact in float32; only the accumulation rounds, a few
+float32 ulps of the bias's scale); bf16 output the float32 value rounded to nearest, so within
+half a bf16 ulp (2^-8 |z|) plus that accumulation error.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+import torch  # noqa: E402
+
+import lossless_draft_verification_sv_amd as sv  # noqa: E402
+import oracle  # noqa: E402
+import workloads  # noqa: E402
+from tests.gpu_util import say, to_dev  # noqa: E402
+
+HERE = os.path.dirname(__file__)
+
+
+def run(base, left, right, anchor, return_logits=True):
+    tok, out = sv.sv_markov_draft(to_dev(base), to_dev(left), to_dev(right),
+                                  None if anchor is None else to_dev(anchor), return_logits)
+    torch.cuda.synchronize()
+    logits = None
+    if out is not None:
+        logits = (out.float() if out.dtype == torch.bfloat16 else out).cpu().numpy()
+    return tok.cpu().numpy(), logits
+
+
+def logit_tol(z, dtype):
+    if dtype == "bf16":
+        return 2.0 ** -8 * np.abs(z) * (1 + 1e-6) + 2e-5
+    return 2e-5 + 1e-6 * np.abs(z)
+
+
+def check_request(name, b, base_b, dtype, left, right, anchor_b, tok_b, logits_b):
+    """One request against markov_draft_request; returns (positions compared, first ambiguous
+    position or None)."""
+    ref_tok, ref_z, gaps = oracle.markov_draft_request(base_b, dtype, left, right, anchor_b)
+    K = ref_tok.shape[0]
+    for k in range(K):
+        if logits_b is not None:
+            err = np.abs(logits_b[k] - ref_z[k])
+            bad = np.nonzero(err > logit_tol(ref_z[k], dtype))[0]
+            assert bad.size == 0, (name, b, k, bad[:5], logits_b[k][bad[:5]], ref_z[k][bad[:5]])
+        if gaps[k] < oracle.AMBIGUOUS_GAP:
+            say(f"[gpu] markov {name}: request {b} position {k} ambiguous (gap {gaps[k]:.2e})")
+            return k + 1, k
+        assert tok_b[k] == ref_tok[k], (name, b, k, tok_b[k], ref_tok[k])
+    return K, None
+
+
+def check_batch(name, base, dtype, left, right, anchor, requests=None, return_logits=True):
+    B, K, V = base.shape
+    say(f"[gpu] markov {name}: B={B} K={K} V={V} R={left.shape[1]} {dtype}")
+    tok, logits = run(base, left, right, anchor, return_logits)
+    assert tok.shape == (B, K)
+    assert np.all((tok >= 0) & (tok < V))
+    idx = range(B) if requests is None else requests
+    n_amb = 0
+    for b in idx:
+        a = -1 if anchor is None else int(anchor[b])
+        _, amb = check_request(name, b, base[b], dtype, left, right, a, tok[b],
+                               None if logits is None else logits[b])
+        n_amb += amb is not None
+    say(f"[gpu] markov {name}: {len(list(idx))} requests checked, {n_amb} ambiguous")
+    return tok, logits
+
+
+def golden_case():
+    g = json.load(open(os.path.join(HERE, "golden", "markov", "of_course.json")))
+    V, R = g["V"], g["R"]
+    Rp = 16  # the kernel's rank is a multiple of 16: pad with zero columns (same products)
+    left = np.zeros((V, Rp), np.float32)
+    right = np.zeros((V, Rp), np.float32)
+    left[:, :R] = np.asarray(g["left_factor"], np.float32)
+    right[:, :R] = np.asarray(g["right_factor"], np.float32)
+    base = np.asarray(g["base_logits"], np.float32)[None]
+    return g, base, workloads.to_bf16_bits(left), workloads.to_bf16_bits(right)
+
+
+def test_golden_of_course():
+    g, base, left, right = golden_case()
+    anchor = np.array([g["anchor"]], np.int32)
+    tok, logits = run(base, left, right, anchor)
+    assert tok[0].tolist() == g["expected"]["tokens"]
+    np.testing.assert_allclose(logits[0], np.asarray(g["expected"]["corrected_logits"]),
+                               rtol=0, atol=1e-6)
+    zero = np.zeros_like(left)
+    tok0, logits0 = run(base, zero, zero, anchor)
+    assert tok0[0].tolist() == g["expected"]["tokens_without_head"]
+    np.testing.assert_array_equal(logits0[0], base[0])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,K,V,R", [
+    (70, 5, 1000, 256),  # two request blocks, ragged; a ragged vocabulary tile
+    (1, 3, 5, 16),       # one tile shorter than a wave
+    (64, 2, 4096, 48),   # rank not a multiple of the operand chunk
+    (3, 4, 300, 1024),   # largest rank
+    (130, 1, 257, 32),   # three request blocks, one position, a one-entry last tile
+])
+def test_markov_parity(dtype, B, K, V, R):
+    base = workloads.markov_base(B, K, V, dtype, seed=11 + B + K)
+    left, right = workloads.markov_factors(V, R, seed=12 + V)
+    rng = np.random.default_rng(13 + B)
+    anchor = rng.integers(0, V, size=B).astype(np.int32)
+    anchor[rng.random(B) < 0.2] = -1       # no bias at position 0
+    anchor[rng.random(B) < 0.1] = V + 3    # outside the vocabulary: no bias either
+    check_batch(f"{dtype} B{B} K{K} V{V} R{R}", base, dtype, left, right, anchor)
+
+
+def test_markov_no_anchor_and_no_logits():
+    B, K, V, R = 9, 4, 777, 64
+    base = workloads.markov_base(B, K, V, "f32", seed=21)
+    left, right = workloads.markov_factors(V, R, seed=22)
+    tok, _ = check_batch("no anchor", base, "f32", left, right, None)
+    tok2, logits2 = run(base, left, right, None, return_logits=False)
+    assert logits2 is None
+    np.testing.assert_array_equal(tok, tok2)
+
+
+def test_markov_vocabulary_of_one():
+    base = np.full((5, 3, 1), -2.5, np.float32)
+    left, right = workloads.markov_factors(1, 16, seed=23)
+    tok, logits = check_batch("V=1", base, "f32", left, right, np.zeros(5, np.int32))
+    assert np.all(tok == 0)
+
+
+def test_markov_zero_factors_is_per_position_argmax():
+    """With a zero head every position takes the argmax of its own base logits (lowest index
+    on ties) and the corrected logits equal the base logits exactly."""
+    B, K, V = 17, 6, 2000
+    base = workloads.markov_base(B, K, V, "bf16", seed=24)
+    base[:, :, 5] = base[:, :, 7] = workloads.to_bf16_bits(np.array([50.0], np.float32))[0]
+    vals_t = workloads.bf16_bits_to_f32(base)  # 50 at 5 and at 7: the lowest index wins
+    zero = np.zeros((V, 32), np.uint16)
+    tok, logits = run(base, zero, zero, np.arange(B, dtype=np.int32))
+    assert np.all(tok == 5)
+    np.testing.assert_array_equal(logits, vals_t)
+    base2 = workloads.markov_base(B, K, V, "bf16", seed=25)
+    tok2, _ = run(base2, zero, zero, None)
+    np.testing.assert_array_equal(tok2, np.argmax(workloads.bf16_bits_to_f32(base2), axis=2))
+
+
+def test_markov_full_size_sampled():
+    """The benchmarked shape (64 requests, 8 positions, Qwen3 vocabulary, rank 256, bf16) in
+    one call; eight requests checked against the oracle one by one."""
+    B, K, V, R = 64, 8, workloads.QWEN3_VOCAB, 256
+    base = workloads.markov_base(B, K, V, "bf16")
+    left, right = workloads.markov_factors(V, R)
+    anchor = np.random.default_rng(26).integers(0, V, size=B).astype(np.int32)
+    check_batch("full", base, "bf16", left, right, anchor, requests=[0, 1, 17, 31, 32, 45, 62, 63])
+
+
+def test_markov_repeat_calls_identical():
+    B, K, V, R = 64, 4, 5000, 256
+    base = workloads.markov_base(B, K, V, "bf16", seed=27)
+    left, right = workloads.markov_factors(V, R, seed=28)
+    anchor = np.arange(B, dtype=np.int32)
+    t1, z1 = run(base, left, right, anchor)
+    t2, z2 = run(base, left, right, anchor)
+    np.testing.assert_array_equal(t1, t2)
+    np.testing.assert_array_equal(z1, z2)

@@ -309,3 +309,26 @@ def schedule_confidences(B: int, K: int, seed: int = 1007) -> np.ndarray:
         c[rng.random(K) < 0.03] = 1.0
         out[b] = c
     return out
+
+
+def markov_factors(V: int, R: int, seed: int = 1008, sigma: float = 0.25):
+    """Synthetic low-rank Markov-head factors [V, R] as bf16 bits (left: row = previous token,
+    right: row = candidate token), N(0, sigma^2) entries: with R = 256 and sigma = 0.25 the
+    bias sum_j L[p, j] * Rf[v, j] has a standard deviation of about 1, the scale of the base
+    logits' noise. The trained factors are not available; these stand in for them."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, V, R]))
+    left = to_bf16_bits(rng.normal(0.0, sigma, size=(V, R)).astype(np.float32))
+    right = to_bf16_bits(rng.normal(0.0, sigma, size=(V, R)).astype(np.float32))
+    return left, right
+
+
+def markov_base(B: int, K: int, V: int, dtype: str = "bf16", seed: int = 1009) -> np.ndarray:
+    """Synthetic base logits [B, K, V] of a parallel drafter, stored as `dtype` (bf16 bits or
+    float32): N(0, 2^2) noise plus one favoured token per position at +6, so that a position
+    has a clear leader that the Markov bias (standard deviation about 1 with markov_factors)
+    overturns now and then."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, B, K, V]))
+    z = rng.normal(0.0, 2.0, size=(B, K, V)).astype(np.float32)
+    lead = rng.integers(0, V, size=(B, K))
+    np.put_along_axis(z, lead[..., None], np.take_along_axis(z, lead[..., None], 2) + 6.0, 2)
+    return _stored(z, dtype)
