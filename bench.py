@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="batched",
-                    help="tiny | interactive | batched | heavy | greedy | mixed | schedule | "
+                    help="tiny | interactive | batched | heavy | greedy | mixed | schedule | markov | "
                          "sweep_<mode>_<K>_<B>_<dtype>")
     ap.add_argument("--min-rotation-bytes", type=float, default=1.2e9,
                     help="rotate input copies until at least this many bytes are cycled")
@@ -79,13 +79,13 @@ def algorithmic_bytes(inp):
     return logits + small, int(ks.sum())
 
 
-def measured_traffic(workload_name):
+def measured_traffic(workload_name, source="sv_kernels.hip"):
     """Calibrated HBM bytes per call from the committed rocprofv3 counter summary of this
     workload, or None when there is none or the kernel source changed since it was taken."""
     import hashlib
 
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload_name}.md")
-    src = os.path.join(ROOT, "lossless_draft_verification_sv_amd", "csrc", "sv_kernels.hip")
+    src = os.path.join(ROOT, "lossless_draft_verification_sv_amd", "csrc", source)
     if not os.path.exists(path):
         return None
     fields = {}
@@ -279,6 +279,92 @@ def bench_schedule(args):
             f.write(json.dumps(result) + "\n")
 
 
+def bench_markov(args):
+    """The Markov-head correction (sv_markov_draft) of a draft block: 64 requests, 8 positions,
+    the Qwen3 vocabulary, rank-256 synthetic bf16 factors, bf16 base logits. Two copies of the
+    base and output logits alternate between steps."""
+    import torch
+
+    import lossless_draft_verification_sv_amd as sv
+    import oracle
+    from workloads import QWEN3_VOCAB, markov_base, markov_factors
+
+    B, K, V, R = 64, 8, QWEN3_VOCAB, 256
+    dev = torch.device("cuda:0")
+    base_h = markov_base(B, K, V, "bf16")
+    left_h, right_h = markov_factors(V, R)
+    anchor_h = np.random.default_rng(1010).integers(0, V, size=B).astype(np.int32)
+
+    def bf16(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    bases = [bf16(base_h) for _ in range(2)]
+    outs = [torch.empty_like(bases[0]) for _ in range(2)]
+    left, right = bf16(left_h), bf16(right_h)
+    anchor = torch.from_numpy(anchor_h).to(dev)
+    tokens = torch.empty(B, K, dtype=torch.int32, device=dev)
+    lib = sv.load_library()
+    stream = torch.cuda.current_stream(dev)
+    ws_bytes = int(lib.sv_markov_workspace_bytes(B, V))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    argv = [[bases[i].data_ptr(), 1, B, K, V, left.data_ptr(), right.data_ptr(), R,
+             anchor.data_ptr(), tokens.data_ptr(), outs[i].data_ptr(), ws.data_ptr(), ws_bytes,
+             stream.cuda_stream] for i in range(2)]
+    for i in range(max(args.warmup, 2)):
+        if lib.sv_markov_draft(*argv[i % 2]) != 0:
+            raise RuntimeError(sv.sv_last_error())
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        lib.sv_markov_draft(*argv[i % 2])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t_start) * 1e3 / args.steps
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    # algorithmic bytes per position: the right factor, the base logits and the corrected logits
+    # (the left rows of the previous tokens, B*R*2 bytes, and the partials are noise)
+    per_pos = V * R * 2 + 2 * B * V * 2
+    gbps = per_pos * K / (us * 1e-6) / 1e9
+    # the oracle on a bounded sample of requests, one by one, its BLAS held to one thread
+    from threadpoolctl import threadpool_limits
+
+    c0 = time.perf_counter()
+    n_req = 0
+    with threadpool_limits(limits=1):
+        while n_req < B:
+            oracle.markov_draft_request(base_h[n_req], "bf16", left_h, right_h,
+                                        int(anchor_h[n_req]))
+            n_req += 1
+            if args.cpu_seconds <= 0 or time.perf_counter() - c0 > args.cpu_seconds:
+                break
+    cpu_s = time.perf_counter() - c0
+    result = {
+        "metric": "Markov-corrected draft positions/s (sv_markov_draft, B*K positions per call)",
+        "value": B * K / (ms_per_step * 1e-3), "unit": "positions/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic N(0, 0.25^2) rank-256 factors and N(0, 2^2) base logits",
+        "config": {"workload": "markov_B64_K8_V151936_R256_bf16", "B": B, "K": K, "V": V,
+                   "R": R},
+        "call_us": {"mean_timed": us},
+        "algorithmic_bytes_per_call": per_pos * K,
+        "roofline": {"bound": "hbm", "kernel": "sv_markov_draft (K markov_stream + K "
+                     "markov_finish launches)", "achieved": gbps, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic("markov_B64_K8_V151936_R256_bf16",
+                                                 "sv_markov.hip")},
+        "cpu_baseline": {"value": n_req * K / cpu_s, "unit": "positions/s", "cores": 1,
+                         "kind": "oracle", "sample": f"{n_req} requests x {K} positions, fp64 "
+                                                     "numpy, one by one"},
+    }
+    print(json.dumps(result), flush=True)
+    if args.out:
+        with open(args.out, "a") as f:
+            f.write(json.dumps(result) + "\n")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -293,6 +379,8 @@ def main():
 
     if args.workload == "schedule":
         return bench_schedule(args)
+    if args.workload == "markov":
+        return bench_markov(args)
     w = pick_workload(args.workload)
     inp = generate(w)
     # the pooled oracle runs first, before this process touches the GPU

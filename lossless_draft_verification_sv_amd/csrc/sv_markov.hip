@@ -203,6 +203,7 @@ __global__ __launch_bounds__(kThreads) void markov_bias_tile(
 constexpr int kStreamTile = 16 * kWaves;     // vocabulary entries per item
 constexpr int kSteps = kRankChunk / 32;      // MFMA steps per item at the largest rank
 constexpr int kZRow = kStreamTile + 4;       // LDS row stride of the corrected tile, in floats
+constexpr int kAhead = 2;                    // items whose operands are in flight
 
 template <typename T>
 struct Base {
@@ -221,6 +222,7 @@ __device__ __forceinline__ float logit_at(const Base<T>& bv, int e) {
 }
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
 // Factor row words of this lane's column of the tile (lane % 16): rank indices
@@ -313,26 +315,42 @@ struct StreamArgs {
   uint64_t* part;
 };
 
-// One item of the staged request block: contract with the factor words in cur (the next
-// item's are requested into nxt first), add the base logits, write the corrected logits and the
-// tile argmax of every request of the block.
+// One item of the staged request block: contract with the factor words in cur (those of the
+// item kAhead on are requested into nxt first), add the base logits, write the corrected logits
+// and the tile argmax of every request of the block.
+template <typename T>
+struct Stage {
+  v4u32 f[kSteps];  // factor row words of this lane's column
+  Base<T> bv;       // base logits this thread finishes
+};
+
+// Requests item j's operands into st (j clamped to the run's last item, so that every trip
+// issues the same loads and the waits stay exact).
 template <typename T, bool VEC>
+__device__ __forceinline__ void load_stage(Stage<T>& st, const StreamArgs& a,
+                                           const T* __restrict__ base, int j, int jend) {
+  j = j < jend ? j : jend - 1;
+  const int tile = j % a.ntile;
+  load_base<T, VEC>(st.bv, base, a.B, a.K, a.V, a.k, tile, (j / a.ntile) * kReqBlock);
+  load_factor(st.f, a.right, a.V, a.R, tile);
+}
+
+template <typename T, bool VEC, bool FULL>
 __device__ __forceinline__ void stream_item(const StreamArgs& a, const T* __restrict__ base,
                                             T* __restrict__ out, uint16_t (*sa)[kARow],
                                             float (*sz)[kZRow], int j, int jend,
-                                            const v4u32 (&cur)[kSteps], v4u32 (&nxt)[kSteps]) {
+                                            const Stage<T>& cur, Stage<T>& nxt) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tile = j % a.ntile, b0 = (j / a.ntile) * kReqBlock;
-  Base<T> bv;
-  load_base<T, VEC>(bv, base, a.B, a.K, a.V, a.k, tile, b0);
-  // unconditional (the last item re-reads its own tile) so that the waits below stay exact
-  load_factor(nxt, a.right, a.V, a.R, (j + 1 < jend ? j + 1 : j) % a.ntile);
+  load_stage<T, VEC>(nxt, a, base, j + kAhead, jend);
+  const Base<T>& bv = cur.bv;
   float4_t acc[4] = {{}, {}, {}, {}};
 #pragma unroll
   for (int t = 0; t < kSteps; ++t) {
-    if (t < a.ns) {  // uniform
-      const bool inside = 4 * t + (lane >> 4) < a.R / 8;
-      const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, inside ? cur[t] : v4u32{0u, 0u, 0u, 0u});
+    if (FULL || t < a.ns) {  // uniform
+      const bool inside = FULL || 4 * t + (lane >> 4) < a.R / 8;
+      const bf16x8_t bfr =
+          __builtin_bit_cast(bf16x8_t, inside ? cur.f[t] : v4u32{0u, 0u, 0u, 0u});
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
         const v4u32 x =
@@ -349,54 +367,66 @@ __device__ __forceinline__ void stream_item(const StreamArgs& a, const T* __rest
     for (int i = 0; i < 4; ++i)
       sz[rb * 16 + 4 * (lane >> 4) + i][wave * 16 + (lane & 15)] = acc[rb][i];
   __syncthreads();
-  // thread (m, q): row m of the block, columns 16 q .. 16 q + 15, ascending
+  // thread (m, q): row m of the block, columns 16 q .. 16 q + 15, ascending; a wave's 16 rows
+  // are rows 16 w .. 16 w + 15, and a wave with no request among them skips the epilogue
   const int m = tid >> 2, q = tid & 3, b = b0 + m;
   const int v0 = tile * kStreamTile + 16 * q;
-  float z[16];
   float best = -INFINITY;
   int bi = INT_MAX;
+  if (b0 + 16 * wave < a.B) {  // uniform over the wave
+    float z[16];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const bool ok = b < a.B && v0 + e < a.V;
-    z[e] = ok ? logit_at<T>(bv, e) + sz[m][16 * q + e] : -INFINITY;
-    if (z[e] > best) {
-      best = z[e];
-      bi = v0 + e;
+    for (int x = 0; x < 4; ++x) {
+      const float4 acc4 = *reinterpret_cast<const float4*>(&sz[m][16 * q + 4 * x]);
+      z[4 * x] = logit_at<T>(bv, 4 * x) + acc4.x;
+      z[4 * x + 1] = logit_at<T>(bv, 4 * x + 1) + acc4.y;
+      z[4 * x + 2] = logit_at<T>(bv, 4 * x + 2) + acc4.z;
+      z[4 * x + 3] = logit_at<T>(bv, 4 * x + 3) + acc4.w;
     }
-  }
-  if (out != nullptr && b < a.B) {
-    T* orow = out + ((size_t)b * a.K + a.k) * (size_t)a.V + v0;
-    if constexpr (VEC) {  // whole vectors: the row ends on a vector boundary
-      constexpr int kVec = Base<T>::kVec;
+    const bool row_ok = b < a.B;
+    const int ncol = a.V - v0;  // columns of this thread inside the vocabulary (may be <= 0)
+    int e_best = -1;
 #pragma unroll
-      for (int w = 0; w < Base<T>::kWords; ++w) {
-        if (v0 + w * kVec < a.V) {
-          if constexpr (sizeof(T) == 4) {
-            *reinterpret_cast<float4*>(orow + 4 * w) =
-                make_float4(z[4 * w], z[4 * w + 1], z[4 * w + 2], z[4 * w + 3]);
-          } else {
-            uint16_t r[8];
+    for (int e = 0; e < 16; ++e) {
+      const bool take = row_ok && e < ncol && z[e] > best;
+      best = take ? z[e] : best;
+      e_best = take ? e : e_best;
+    }
+    bi = e_best < 0 ? INT_MAX : v0 + e_best;
+    if (out != nullptr && row_ok) {
+      T* orow = out + ((size_t)b * a.K + a.k) * (size_t)a.V + v0;
+      if constexpr (VEC) {  // whole vectors: the row ends on a vector boundary
+        constexpr int kVec = Base<T>::kVec;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) Logit<T>::put(&r[e], z[8 * w + e]);
-            *reinterpret_cast<v4u32*>(orow + 8 * w) =
-                v4u32{r[0] | ((uint32_t)r[1] << 16), r[2] | ((uint32_t)r[3] << 16),
-                      r[4] | ((uint32_t)r[5] << 16), r[6] | ((uint32_t)r[7] << 16)};
+        for (int w = 0; w < Base<T>::kWords; ++w) {
+          if (w * kVec < ncol) {
+            if constexpr (sizeof(T) == 4) {
+              *reinterpret_cast<float4*>(orow + 4 * w) =
+                  make_float4(z[4 * w], z[4 * w + 1], z[4 * w + 2], z[4 * w + 3]);
+            } else {  // round to nearest even
+              uint32_t r[4];
+#pragma unroll
+              for (int x = 0; x < 4; ++x)
+                r[x] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)z[8 * w + 2 * x],
+                                                             (__bf16)z[8 * w + 2 * x + 1]});
+              *reinterpret_cast<v4u32*>(orow + 8 * w) = v4u32{r[0], r[1], r[2], r[3]};
+            }
           }
         }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (e < ncol) Logit<T>::put(orow + e, z[e]);
       }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (v0 + e < a.V) Logit<T>::put(orow + e, z[e]);
     }
-  }
 #pragma unroll
-  for (int s = 1; s <= 2; s <<= 1) {
-    const float b2 = __shfl_xor(best, s);
-    const int i2 = __shfl_xor(bi, s);
-    if (better(b2, i2, best, bi)) {
-      best = b2;
-      bi = i2;
+    for (int s = 1; s <= 2; s <<= 1) {
+      const float b2 = __shfl_xor(best, s);
+      const int i2 = __shfl_xor(bi, s);
+      if (better(b2, i2, best, bi)) {
+        best = b2;
+        bi = i2;
+      }
     }
   }
   if (q == 0 && b < a.B)
@@ -404,8 +434,8 @@ __device__ __forceinline__ void stream_item(const StreamArgs& a, const T* __rest
   __syncthreads();  // sz is rewritten by the next item
 }
 
-template <typename T, bool VEC>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void markov_stream(const T* __restrict__ base,
+template <typename T, bool VEC, bool FULL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void markov_stream(const T* __restrict__ base,
                                                           T* __restrict__ out, StreamArgs a,
                                                           int nrb, int per_group) {
   __shared__ __attribute__((aligned(16))) uint16_t sa[kReqBlock][kARow];
@@ -414,21 +444,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const int w = (int)(blockIdx.x & 7) * lanes8 + (int)(blockIdx.x >> 3);
   const int j0 = w * per_group, j1 = j0 + per_group < n ? j0 + per_group : n;
   if (j0 >= j1) return;  // uniform over the work-group
-  v4u32 f0[kSteps], f1[kSteps];
+  Stage<T> s0, s1, s2;
   for (int j = j0; j < j1;) {  // runs of items that share a request block
     const int rbk = j / a.ntile;
     const int jend = (rbk + 1) * a.ntile < j1 ? (rbk + 1) * a.ntile : j1;
-    {  // previous tokens first, then the first item's factor words, then the left rows
+    {  // previous tokens first, then the first items' operands, then the left rows
       int p[kReqBlock / 8];
       stage_tokens(p, a.prev_tok, a.prev_stride, a.B, a.V, rbk * kReqBlock);
-      load_factor(f0, a.right, a.V, a.R, j % a.ntile);
+      load_stage<T, VEC>(s0, a, base, j, jend);
+      load_stage<T, VEC>(s1, a, base, j + 1, jend);
       if (j > j0) __syncthreads();  // the previous block's rows are no longer read
       stage_rows(sa, p, a.left, a.R);
     }
-    for (; j < jend; j += 2) {  // two items per trip, the factor buffers alternating
-      stream_item<T, VEC>(a, base, out, sa, sz, j, jend, f0, f1);
-      if (j + 1 < jend) stream_item<T, VEC>(a, base, out, sa, sz, j + 1, jend, f1, f0);
+    // three items per trip, the operand stages rotating; whole trips only, so that the loads
+    // still in flight at the loop's back edge are always the same two stages
+    for (; j + 3 <= jend; j += 3) {
+      stream_item<T, VEC, FULL>(a, base, out, sa, sz, j, jend, s0, s2);
+      stream_item<T, VEC, FULL>(a, base, out, sa, sz, j + 1, jend, s1, s0);
+      stream_item<T, VEC, FULL>(a, base, out, sa, sz, j + 2, jend, s2, s1);
     }
+    if (j < jend) stream_item<T, VEC, FULL>(a, base, out, sa, sz, j, jend, s0, s2);
+    if (j + 1 < jend) stream_item<T, VEC, FULL>(a, base, out, sa, sz, j + 1, jend, s1, s0);
+    j = jend;
   }
 }
 
@@ -509,22 +546,30 @@ int launch_all(const void* base, void* out, int B, int K, int V, const uint16_t*
   const int ntile = stream ? (V + kStreamTile - 1) / kStreamTile : (V + kTileV - 1) / kTileV;
   const int n = ntile * nrb;
   const int groups = 8 * ((n + 7) / 8);
-  // persistent form: up to three work-groups per CU, each a contiguous run of equally many items
-  const int slots = 3 * cu_count();
+  const bool vec_rows = aligned16(base) && aligned16(out) && ((size_t)V * sizeof(T)) % 16 == 0;
+  // persistent form: as many work-groups as are resident at once, each a contiguous run of
+  // equally many items
+  const bool full = R == kRankChunk;
+  const void* fn = full ? (vec_rows ? reinterpret_cast<const void*>(&markov_stream<T, true, true>)
+                                    : reinterpret_cast<const void*>(&markov_stream<T, false, true>))
+                        : (vec_rows ? reinterpret_cast<const void*>(&markov_stream<T, true, false>)
+                                    : reinterpret_cast<const void*>(&markov_stream<T, false, false>));
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  const int slots = per_cu * cu_count();
   const int per = (n + slots - 1) / slots;
   const int pgroups = 8 * (((n + per - 1) / per + 7) / 8);
-  const bool vec_rows = aligned16(base) && aligned16(out) && ((size_t)V * sizeof(T)) % 16 == 0;
   for (int k = 0; k < K; ++k) {
     const int32_t* prev = k == 0 ? anchor : tokens + (k - 1);
     const int stride = k == 0 ? 1 : K;
     if (stream) {
       const StreamArgs a{B, K, V, k, R, (R + 31) / 32, ntile, stride, left, right, prev, part};
-      if (vec_rows)
-        hipLaunchKernelGGL((markov_stream<T, true>), dim3(pgroups), dim3(kThreads), 0, s,
-                           static_cast<const T*>(base), static_cast<T*>(out), a, nrb, per);
-      else
-        hipLaunchKernelGGL((markov_stream<T, false>), dim3(pgroups), dim3(kThreads), 0, s,
-                           static_cast<const T*>(base), static_cast<T*>(out), a, nrb, per);
+      hipLaunchKernelGGL(reinterpret_cast<void (*)(const T*, T*, StreamArgs, int, int)>(
+                             const_cast<void*>(fn)),
+                         dim3(pgroups), dim3(kThreads), 0, s, static_cast<const T*>(base),
+                         static_cast<T*>(out), a, nrb, per);
     } else {
       hipLaunchKernelGGL(markov_bias_tile<T>, dim3(groups), dim3(kThreads), 0, s,
                          static_cast<const T*>(base), static_cast<T*>(out), B, K, V, k, left,
