@@ -2,7 +2,11 @@
 
 Checked against the pages' worked example (tests/golden/markov/of_course.json), closed forms
 (zero factors leave the base logits; rank-1 factors give a_prev * b_v), a brute-force double
-loop for the bias, and the anchor rule. Planted mistakes must be caught.
+loop for the bias, and the anchor rule. The top-K variant: the same example with 1, 2 and all
+candidates (tests/golden/markov/of_course_topk.json: one candidate changes the proposal, as the
+pages say candidate limiting can), kc = V equal to the full head, a brute-force sort for the
+selection (ties, NaN, -inf), and a bias that would lift a non-candidate. Planted mistakes must be
+caught.
 """
 import json
 import os
@@ -101,8 +105,70 @@ def check_ties_lowest_index():
     assert amb[0]
 
 
+def check_topk_golden():
+    g = json.load(open(os.path.join(HERE, "golden", "markov", "of_course_topk.json")))
+    base = np.asarray(g["base_logits"], np.float32)
+    L, R = bits(g["left_factor"]), bits(g["right_factor"])
+    for kc, want in g["expected"].items():
+        t, c, z, _ = M.markov_topk_request(base, "f32", L, R, g["anchor"], int(kc))
+        assert t.tolist() == want["tokens"], kc
+        assert c.tolist() == want["candidates"], kc
+        assert np.allclose(z, want["corrected"]), kc
+
+
+def check_topk_full_vocabulary_is_the_head():
+    rng = np.random.default_rng(6)
+    K, V, R = 5, 23, 6
+    base = to_bf16_bits(rng.normal(0, 1, size=(K, V)).astype(np.float32))
+    L = bits(rng.normal(0, 1, size=(V, R)))
+    Rf = bits(rng.normal(0, 1, size=(V, R)))
+    for anchor in (-1, 3):
+        t, c, z, _ = M.markov_topk_request(base, "bf16", L, Rf, anchor, V)
+        tf, cf, _ = M.markov_draft_request(base, "bf16", L, Rf, anchor)
+        assert np.array_equal(t, tf)
+        assert np.array_equal(c, np.tile(np.arange(V), (K, 1)))
+        assert np.array_equal(z, cf)
+
+
+def check_topk_selection_bruteforce():
+    rng = np.random.default_rng(7)
+    for trial in range(200):
+        V = int(rng.integers(1, 40))
+        z = rng.choice([-2.0, -1.0, 0.0, 0.5, 1.0, 3.0], size=V)  # many ties
+        z[rng.random(V) < 0.1] = np.nan
+        z[rng.random(V) < 0.1] = -np.inf
+        kc = int(rng.integers(1, V + 1))
+        order = sorted(range(V), key=lambda v: (bool(np.isnan(z[v])),
+                                                0.0 if np.isnan(z[v]) else -z[v], v))
+        assert M.topk_candidates(z, kc).tolist() == sorted(order[:kc]), (z, kc)
+        if kc < V:  # nested: one more candidate keeps every earlier one
+            assert set(M.topk_candidates(z, kc)) <= set(M.topk_candidates(z, kc + 1))
+
+
+def check_topk_zero_head_and_restriction():
+    rng = np.random.default_rng(8)
+    K, V = 3, 30
+    base = rng.normal(0, 1, size=(K, V)).astype(np.float32)
+    zero = bits(np.zeros((V, 4)))
+    t, c, z, _ = M.markov_topk_request(base, "f32", zero, zero, 2, 4)
+    assert t.tolist() == [int(np.argmax(base[k])) for k in range(K)]
+    assert np.array_equal(z, np.take_along_axis(base.astype(np.float64), c, 1))
+    # a bias that lifts a token outside the candidates: the full head takes it, top-K cannot
+    base = np.zeros((2, 6), np.float32)
+    base[:, 0] = 1.0
+    base[:, 1] = 0.9
+    Lm = np.zeros((6, 1), np.float32)
+    Lm[0, 0] = 1.0
+    Rm = np.zeros((6, 1), np.float32)
+    Rm[5, 0] = 4.0
+    tf, _, _ = M.markov_draft_request(base, "f32", bits(Lm), bits(Rm), -1)
+    tk, ck, _, _ = M.markov_topk_request(base, "f32", bits(Lm), bits(Rm), -1, 2)
+    assert tf.tolist() == [0, 5] and tk.tolist() == [0, 0] and ck[1].tolist() == [0, 1]
+
+
 CHECKS = [check_golden, check_closed_forms, check_bruteforce_bias, check_anchor_rule,
-          check_ties_lowest_index]
+          check_ties_lowest_index, check_topk_golden, check_topk_full_vocabulary_is_the_head,
+          check_topk_selection_bruteforce, check_topk_zero_head_and_restriction]
 
 
 @pytest.mark.parametrize("chk", CHECKS, ids=lambda f: f.__name__)
@@ -114,9 +180,22 @@ SRC = open(real.__file__).read()
 MUTATIONS = {
     "factors_swapped": ("z = z + Rf @ L[prev]", "z = z + L @ Rf[prev]"),
     "bias_from_own_position": ("        prev = y\n", "        prev = prev\n"),
-    "no_anchor_bias": ("    prev = int(anchor)\n", "    prev = -1\n"),
+    "no_anchor_bias": (
+        "    prev = int(anchor)\n    for k in range(K):\n        z = decode_logits(base[k], dtype).copy()",
+        "    prev = -1\n    for k in range(K):\n        z = decode_logits(base[k], dtype).copy()"),
+    "topk_no_anchor_bias": (
+        "    prev = int(anchor)\n    for k in range(K):\n        z = decode_logits(base[k], dtype)\n",
+        "    prev = -1\n    for k in range(K):\n        z = decode_logits(base[k], dtype)\n"),
     "bias_sign_flipped": ("z = z + Rf @ L[prev]", "z = z - Rf @ L[prev]"),
     "ties_highest_index": ("y = argmax_lowest(z)", "y = int(len(z) - 1 - np.argmax(z[::-1]))"),
+    "topk_ties_to_higher_index": ("order = np.lexsort((np.arange(z.shape[0]),",
+                                  "order = np.lexsort((-np.arange(z.shape[0]),"),
+    "topk_nan_preferred": ("-np.where(nan, 0.0, z), nan))", "-np.where(nan, 0.0, z), ~nan))"),
+    "topk_candidates_from_corrected": ("cand = topk_candidates(z, kc)",
+                                       "cand = topk_candidates(z + (Rf @ L[prev] if 0 <= prev < V "
+                                       "else 0.0), kc)"),
+    "topk_bias_wrong_rows": ("zc = zc + Rf[cand] @ L[prev]", "zc = zc + Rf[:kc] @ L[prev]"),
+    "topk_token_is_position": ("tokens[k] = int(cand[j])", "tokens[k] = int(j)"),
 }
 
 
