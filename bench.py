@@ -34,6 +34,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="batched",
                     help="tiny | interactive | batched | heavy | greedy | mixed | schedule | markov | "
+                         "markov_topk | "
                          "sweep_<mode>_<K>_<B>_<dtype>")
     ap.add_argument("--min-rotation-bytes", type=float, default=1.2e9,
                     help="rotate input copies until at least this many bytes are cycled")
@@ -365,6 +366,92 @@ def bench_markov(args):
             f.write(json.dumps(result) + "\n")
 
 
+def bench_markov_topk(args):
+    """Top-K Markov drafting (sv_markov_topk): 64 requests, 8 positions, the Qwen3 vocabulary,
+    rank-256 synthetic bf16 factors, 64 candidates per position, bf16 base logits. Two copies of
+    the base logits alternate between steps."""
+    import torch
+
+    import lossless_draft_verification_sv_amd as sv
+    import oracle
+    from workloads import QWEN3_VOCAB, markov_base, markov_factors
+
+    B, K, V, R, KC = 64, 8, QWEN3_VOCAB, 256, 64
+    dev = torch.device("cuda:0")
+    base_h = markov_base(B, K, V, "bf16")
+    left_h, right_h = markov_factors(V, R)
+    anchor_h = np.random.default_rng(1010).integers(0, V, size=B).astype(np.int32)
+
+    def bf16(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    bases = [bf16(base_h) for _ in range(2)]
+    left, right = bf16(left_h), bf16(right_h)
+    anchor = torch.from_numpy(anchor_h).to(dev)
+    tokens = torch.empty(B, K, dtype=torch.int32, device=dev)
+    cands = torch.empty(B, K, KC, dtype=torch.int32, device=dev)
+    logits = torch.empty(B, K, KC, dtype=torch.float32, device=dev)
+    lib = sv.load_library()
+    stream = torch.cuda.current_stream(dev)
+    ws_bytes = int(lib.sv_markov_topk_workspace_bytes(B, K, V))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    argv = [[bases[i].data_ptr(), 1, B, K, V, left.data_ptr(), right.data_ptr(), R, KC,
+             anchor.data_ptr(), tokens.data_ptr(), cands.data_ptr(), logits.data_ptr(),
+             ws.data_ptr(), ws_bytes, stream.cuda_stream] for i in range(2)]
+    for i in range(max(args.warmup, 2)):
+        if lib.sv_markov_topk(*argv[i % 2]) != 0:
+            raise RuntimeError(sv.sv_last_error())
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        lib.sv_markov_topk(*argv[i % 2])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t_start) * 1e3 / args.steps
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    # algorithmic bytes per call: every base logit once, and the left and right factor rows of
+    # every candidate (B*K*KC rows of R bf16 each); outputs and tables are small
+    per_call = B * K * V * 2 + 2 * B * K * KC * R * 2
+    gbps = per_call / (us * 1e-6) / 1e9
+    from threadpoolctl import threadpool_limits
+
+    c0 = time.perf_counter()
+    n_req = 0
+    with threadpool_limits(limits=1):
+        while n_req < B:
+            oracle.markov_topk_request(base_h[n_req], "bf16", left_h, right_h,
+                                       int(anchor_h[n_req]), KC)
+            n_req += 1
+            if args.cpu_seconds <= 0 or time.perf_counter() - c0 > args.cpu_seconds:
+                break
+    cpu_s = time.perf_counter() - c0
+    result = {
+        "metric": "top-K Markov draft positions/s (sv_markov_topk, B*K positions per call)",
+        "value": B * K / (ms_per_step * 1e-3), "unit": "positions/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic N(0, 0.25^2) rank-256 factors and N(0, 2^2) base logits",
+        "config": {"workload": "markov_topk_B64_K8_V151936_R256_kc64_bf16", "B": B, "K": K,
+                   "V": V, "R": R, "kc": KC},
+        "call_us": {"mean_timed": us},
+        "algorithmic_bytes_per_call": per_call,
+        "roofline": {"bound": "hbm", "kernel": "sv_markov_topk (topk_chunk + topk_merge + "
+                     "topk_bias + topk_walk)", "achieved": gbps, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic("markov_topk_B64_K8_V151936_R256_kc64_bf16",
+                                                 "sv_markov_topk.hip")},
+        "cpu_baseline": {"value": n_req * K / cpu_s, "unit": "positions/s", "cores": 1,
+                         "kind": "oracle", "sample": f"{n_req} requests x {K} positions, fp64 "
+                                                     "numpy, one by one"},
+    }
+    print(json.dumps(result), flush=True)
+    if args.out:
+        with open(args.out, "a") as f:
+            f.write(json.dumps(result) + "\n")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -381,6 +468,8 @@ def main():
         return bench_schedule(args)
     if args.workload == "markov":
         return bench_markov(args)
+    if args.workload == "markov_topk":
+        return bench_markov_topk(args)
     w = pick_workload(args.workload)
     inp = generate(w)
     # the pooled oracle runs first, before this process touches the GPU

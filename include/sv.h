@@ -210,6 +210,31 @@ int sv_markov_draft(const void* base_logits, int dtype, int B, int K, int V,
                     const int32_t* anchor, int32_t* draft_tokens, void* draft_logits,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Top-K Markov drafting ("Bringing DSpark to vLLM Metal", Making the draft cheaper): per draft
+ * position the candidates are the kc largest base logits (NaN below every number, ties to the
+ * lower index), and the Markov correction of sv_markov_draft is applied to those rows only:
+ *   z[b][k][j] = base[b][k][c_j] + L[prev] . Rf[c_j],   c = the position's candidates in
+ *   ascending vocabulary order, prev = the anchor at k = 0 (no bias when NULL or outside
+ *   [0, V)), else the token chosen at k-1;  token = the c_j with the largest z (lowest index on
+ *   ties). With kc = V this is sv_markov_draft restricted to its tokens.
+ *
+ *  base_logits   [B, K, V] dtype, device; left_factor, right_factor [V, R] bf16, 16-byte aligned
+ *  R             a multiple of 16 in [16, 256];  kc  candidates, 1 <= kc <= min(64, V)
+ *  anchor        [B] int32 device or NULL
+ *  draft_tokens  [B, K] int32 out;  candidates [B, K, kc] int32 out or NULL (ascending index)
+ *  cand_logits   [B, K, kc] float out or NULL: the corrected logits z of the candidates
+ *  workspace     sv_markov_topk_workspace_bytes(B, K, V) bytes, 256-byte aligned, device; no
+ *                clearing needed (left holding intermediate tables, not tagged words)
+ * Four launches on `stream`. Returns SV_OK, SV_ERR_INVALID_ARG, SV_ERR_UNSUPPORTED (more than
+ * 2048 chunk candidates per row: ceil(V / 16384) * kc; 524288 entries at kc = 64),
+ * SV_ERR_WORKSPACE or SV_ERR_HIP; nothing is launched unless SV_OK.
+ */
+size_t sv_markov_topk_workspace_bytes(int B, int K, int V);
+int sv_markov_topk(const void* base_logits, int dtype, int B, int K, int V,
+                   const uint16_t* left_factor, const uint16_t* right_factor, int R, int kc,
+                   const int32_t* anchor, int32_t* draft_tokens, int32_t* candidates,
+                   float* cand_logits, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Read probe (a measurement aid, not a step of the method): the plainest stream over a device
  * buffer, so that the row stream can be compared with the read bandwidth this device reaches.
  * `groups` work-groups of 256 threads read every 16-byte word of data[0, bytes) once with

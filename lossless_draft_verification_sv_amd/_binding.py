@@ -69,6 +69,11 @@ def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
         lib.sv_markov_draft.argtypes = [vp, i32, i32, i32, i32, vp, vp, i32, vp, vp, vp, vp, sz,
                                         vp]
         lib.sv_markov_draft.restype = i32
+        lib.sv_markov_topk_workspace_bytes.argtypes = [i32, i32, i32]
+        lib.sv_markov_topk_workspace_bytes.restype = sz
+        lib.sv_markov_topk.argtypes = [vp, i32, i32, i32, i32, vp, vp, i32, i32, vp, vp, vp, vp,
+                                       vp, sz, vp]
+        lib.sv_markov_topk.restype = i32
         lib.sv_read_probe.argtypes = [vp, sz, vp, i32, vp]
         lib.sv_read_probe.restype = i32
         _lib = lib
@@ -322,6 +327,44 @@ def sv_markov_draft(base: torch.Tensor, left_factor: torch.Tensor, right_factor:
                                _ptr(right_factor), R, _ptr(anchor), _ptr(tokens), _ptr(out),
                                _ptr(ws), ws.numel(), stream))
     return tokens, out
+
+
+class TopkOutput(NamedTuple):
+    tokens: torch.Tensor  # [B, K] int32
+    candidates: Optional[torch.Tensor]  # [B, K, kc] int32, ascending vocabulary index
+    cand_logits: Optional[torch.Tensor]  # [B, K, kc] float32 corrected logits
+
+
+def sv_markov_topk(base: torch.Tensor, left_factor: torch.Tensor, right_factor: torch.Tensor,
+                   kc: int, anchor: Optional[torch.Tensor] = None,
+                   return_candidates: bool = True) -> TopkOutput:
+    """Top-K Markov drafting on the tensors' GPU (see sv_markov_topk in include/sv.h)."""
+    lib = load_library()
+    if base.dim() != 3:
+        raise ValueError("base must be [B, K, V]")
+    B, K, V = base.shape
+    dev = base.device
+    if dev.type != "cuda":
+        raise ValueError("base must be a GPU tensor")
+    _need(base, "base", base.dtype, (B, K, V), dev)
+    if left_factor.dim() != 2:
+        raise ValueError("left_factor must be [V, R]")
+    R = left_factor.shape[1]
+    _need(left_factor, "left_factor", torch.bfloat16, (V, R), dev)
+    _need(right_factor, "right_factor", torch.bfloat16, (V, R), dev)
+    if anchor is not None:
+        _need(anchor, "anchor", torch.int32, (B,), dev)
+    kc = int(kc)
+    tokens = torch.empty(B, K, dtype=torch.int32, device=dev)
+    cands = torch.empty(B, K, kc, dtype=torch.int32, device=dev) if return_candidates else None
+    logits = torch.empty(B, K, kc, dtype=torch.float32, device=dev) if return_candidates else None
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    nbytes = int(lib.sv_markov_topk_workspace_bytes(B, K, V))
+    ws = _workspace(dev, stream, nbytes, "markov")
+    _check(lib.sv_markov_topk(_ptr(base), _dtype_code(base), B, K, V, _ptr(left_factor),
+                              _ptr(right_factor), R, kc, _ptr(anchor), _ptr(tokens), _ptr(cands),
+                              _ptr(logits), _ptr(ws), ws.numel(), stream))
+    return TopkOutput(tokens, cands, logits)
 
 
 def sv_read_probe(data: torch.Tensor, groups: int = 2048) -> torch.Tensor:

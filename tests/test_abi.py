@@ -221,3 +221,22 @@ def test_markov_rejects_invalid_arguments(lib, kw, status):
     args.update(kw)
     assert lib.sv_markov_draft(*args.values()) == status
     assert sv.sv_last_error() != ""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), sv.SV_ERR_INVALID_ARG), (dict(K=65), sv.SV_ERR_INVALID_ARG),
+    (dict(V=0), sv.SV_ERR_INVALID_ARG), (dict(dtype=9), sv.SV_ERR_INVALID_ARG),
+    (dict(R=264), sv.SV_ERR_INVALID_ARG), (dict(R=272), sv.SV_ERR_INVALID_ARG),
+    (dict(kc=0), sv.SV_ERR_INVALID_ARG), (dict(kc=65), sv.SV_ERR_INVALID_ARG),
+    (dict(V=10, kc=11), sv.SV_ERR_INVALID_ARG), (dict(V=1 << 26, kc=64), sv.SV_ERR_UNSUPPORTED),
+    (dict(base=None), sv.SV_ERR_INVALID_ARG), (dict(tokens=None), sv.SV_ERR_INVALID_ARG),
+    (dict(right=FAKE + 4), sv.SV_ERR_INVALID_ARG), (dict(ws=None), sv.SV_ERR_WORKSPACE),
+    (dict(ws_bytes=8), sv.SV_ERR_WORKSPACE), (dict(ws=WS + 16), sv.SV_ERR_WORKSPACE),
+])
+def test_markov_topk_rejects_invalid_arguments(lib, kw, status):
+    args = dict(base=FAKE, dtype=sv.SV_DTYPE_BF16, B=4, K=4, V=1000, left=FAKE, right=FAKE,
+                R=256, kc=64, anchor=None, tokens=FAKE, cands=None, logits=None, ws=WS,
+                ws_bytes=1 << 40, stream=None)
+    args.update(kw)
+    assert lib.sv_markov_topk(*args.values()) == status
+    assert sv.sv_last_error() != ""
