@@ -64,6 +64,8 @@ constexpr int kStageMax = 2048;   // partials of one request staged in LDS: (2K+
 constexpr int kChunkTiles = 512;  // draw tiles per draw group, at most
 constexpr int kMaxC2 = 512;       // draw groups per request, at most
 constexpr int kDrawGroups = 1024;  // draw groups per launch the plan aims at
+constexpr int kSegGroups = 64 * kUnroll;  // groups per segment of a bonus row: one wave's round
+constexpr int kSegMax = 1024;     // segments per bonus row, at most (else the tile draw is used)
 constexpr int kLaneRowChunks = 32;  // up to this many chunks per row, one lane combines a row
 constexpr int kSpinLimit = 1 << 21;  // polls (about 1 us each) before a waiting group gives up
 constexpr int32_t kTimedOut = -2;    // accepted_len value reported by a group that gave up
@@ -77,6 +79,7 @@ struct Plan {
   int NT;  // draw tiles per request: ceil(V / 512)
   int C2;  // vocabulary chunks per request, draw groups
   int Cg;  // vocabulary chunks per row, greedy
+  int NSmax;  // segment slots per request in the workspace: min(ceil(V / 64), kSegMax)
 };
 
 int chunks_for(long rows, long units, long target_groups, long min_units, int max_chunks) {
@@ -103,6 +106,8 @@ Plan make_plan(int B, int K, int V) {
   const int need = (p.NT + kChunkTiles - 1) / kChunkTiles;
   if (p.C2 < need) p.C2 = need;
   p.Cg = chunks_for((long)B * (K + 1), V, 8192, 4096, kStageMax / (K + 1));
+  const long ns = ((long)V + kSegGroups - 1) / kSegGroups;
+  p.NSmax = (int)(ns < kSegMax ? ns : kSegMax);
   return p;
 }
 
@@ -119,6 +124,7 @@ struct Layout {
   size_t stats;   // uint64 [B][2K+1][C][2]  row-stat partials: tagged offset, tagged sum
   size_t gath;    // uint64 [B][K][2]        tagged logits at draft token i: target row, draft row
   size_t ctot;    // uint64 [B][C2][2]       tagged draw chunk totals (fp64 high, low halves)
+  size_t seg;     // uint64 [B][NSmax][2]    tagged segment partials of each request's bonus row
   size_t gstats;  // uint64 [B][K+1][Cg][2]  greedy partials: tagged value, tagged index
   size_t total;
 };
@@ -134,6 +140,8 @@ Layout make_layout(int B, int K, int V, const Plan& p) {
   off = align_up(off + 8 * (size_t)B * 2 * K, 256);
   L.ctot = off;
   off = align_up(off + 16 * (size_t)B * p.C2, 256);
+  L.seg = off;
+  off = align_up(off + 16 * (size_t)B * p.NSmax, 256);
   L.gstats = 0;  // greedy calls reuse the front of the workspace
   const size_t g = align_up(16 * (size_t)B * (K + 1) * p.Cg, 256);
   L.total = off > g ? off : g;
@@ -220,6 +228,22 @@ __device__ __forceinline__ int wave_max_i32(int x) {
   SV_SCAN_STEPS(SV_MAX_STEP);
 #undef SV_MAX_STEP
   return (int)lane_u32((uint32_t)x, 63);
+}
+
+// Sum over the wave in fp32, wave-uniform: a tree of depth 6 (relative error <= 6 ulp).
+__device__ __forceinline__ float wave_sum_f32(float x) {
+#define SV_FADD_STEP(CTRL, ROWS) x += dpp_f32<CTRL, ROWS>(x, 0.0f)
+  SV_SCAN_STEPS(SV_FADD_STEP);
+#undef SV_FADD_STEP
+  return lane_f32(x, 63);
+}
+
+// Maximum over the wave, wave-uniform (NaN-free inputs give the largest; -inf the identity).
+__device__ __forceinline__ float wave_max_f32(float x) {
+#define SV_FMAX_STEP(CTRL, ROWS) x = fmaxf(x, dpp_f32<CTRL, ROWS>(x, -INFINITY))
+  SV_SCAN_STEPS(SV_FMAX_STEP);
+#undef SV_FMAX_STEP
+  return lane_f32(x, 63);
 }
 
 // Awaits up to four tagged word pairs (p[u], p[u] + 1), those with live[u]: loads them all, then
@@ -549,6 +573,9 @@ struct SampleArgs {
   uint64_t* stats;
   uint64_t* gath;  // [B][K][2]
   uint64_t* ctot;
+  uint64_t* seg;  // [B][NSmax][2]
+  int NS;         // segments of a bonus row, or 0: bonus tokens are drawn like residual ones
+  int NSmax;
   int32_t* accepted_len;
   int32_t* committed;
   float* target_prob;
@@ -604,6 +631,115 @@ __device__ __forceinline__ Req<T> request_of(const SampleArgs& a, int b) {
   return q;
 }
 
+// Bonus row of a request (target row k_b, the row the token after an all-accepted block is drawn
+// from). Streamed like the other rows, except that a wave's round of kUnroll loads covers one run
+// of kSegGroups consecutive groups (load j: 64 groups at 64 j), a segment, and that each round's
+// offset is one for the whole wave. So every round also gives its segment's sum of
+// 2^(fma(z, c, -o)), which is published with its offset: segment s covers groups
+// [s kSegGroups, (s + 1) kSegGroups), and the chunk bounds of a bonus row are multiples of
+// kSegGroups. The draw then locates p_k's inverse CDF down to one segment without a second pass
+// over the row. Sums are fp32 trees: over a load's E elements, over the kUnroll loads, then over
+// the wave (depth 3 + 2 + 6), so a segment sum is within 11 ulp (relative) of the exact sum of its
+// fp32 weights, and the inverse CDF built from them is off by less than 7e-7 of the row's mass.
+// Loads of groups past g1 are clamped to g1 - 1 and masked to -inf, so every round issues the
+// same loads and every lane takes part in the wave reductions.
+template <typename T, bool VEC>
+struct SegBuf {
+  typename Rows<T, VEC>::Raw a[kUnroll];
+  // Round starting at group `seg`, the first group of this wave's segment.
+  __device__ __forceinline__ void load(const T* __restrict__ row, int seg, int g1) {
+    const int g = seg + (int)(threadIdx.x & 63);
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const int gj = g + 64 * j;
+      a[j] = Rows<T, VEC>::load(row, gj < g1 ? gj : g1 - 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+};
+
+template <typename T, bool VEC>
+__device__ __forceinline__ void seg_round(const SegBuf<T, VEC>& x, int seg, int g1, float c,
+                                          float& o, float& s, uint64_t* segs, uint32_t tag) {
+  constexpr int E = Rows<T, VEC>::E;
+  const int g = seg + (int)(threadIdx.x & 63);
+  float f[kUnroll][E];
+  float bm = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kUnroll; ++j) {
+    Rows<T, VEC>::unpack(x.a[j], f[j]);
+    const bool ok = g + 64 * j < g1;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      f[j][e] = ok ? f[j][e] : -INFINITY;
+      bm = fmaxf(bm, f[j][e]);
+    }
+  }
+  const float on = fmaxf(o, ceilf(wave_max_f32(bm) * c));
+  s = rescale(s, o, on);
+  o = on;
+  float x4[kUnroll];
+#pragma unroll
+  for (int j = 0; j < kUnroll; ++j) {
+    float x[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = __builtin_amdgcn_exp2f(fmaf(f[j][e], c, -o));
+#pragma unroll
+    for (int h = 1; h < E; h *= 2)
+#pragma unroll
+      for (int e = 0; e + h < E; e += 2 * h) x[e] += x[e + h];
+    x4[j] = x[0];
+  }
+#pragma unroll
+  for (int h = 1; h < kUnroll; h *= 2)
+#pragma unroll
+    for (int j = 0; j + h < kUnroll; j += 2 * h) x4[j] += x4[j + h];
+  s += x4[0];
+  const float st = wave_sum_f32(x4[0]);
+  if ((threadIdx.x & 63) == 0 && seg < g1) {
+    uint64_t* w = segs + (seg / kSegGroups) * 2;
+    publish(w, tag, __float_as_uint(o));
+    publish(w + 1, tag, __float_as_uint(st));
+  }
+}
+
+// Streams groups [g0, g1) of a bonus row (g0 a multiple of kSegGroups) into the thread's (o, s),
+// publishing the segment partials on the way. Rounds of kBlock * kUnroll groups (wave w takes
+// the w-th segment of the round), two register sets in turn, as in stream_groups.
+template <typename T, bool VEC>
+__device__ __forceinline__ void stream_segments(const T* __restrict__ row, int g0, int g1, float c,
+                                                uint64_t* segs, uint32_t tag, float& o, float& s) {
+  constexpr int step = kUnroll * kBlock;
+  const int rounds = (g1 - g0 + step - 1) / step;
+  const int seg = g0 + kSegGroups * (int)(threadIdx.x >> 6);
+  o = -FLT_MAX;
+  s = 0.0f;
+  if (rounds <= 0) return;
+  SegBuf<T, VEC> x, y;
+  x.load(row, seg, g1);
+  int r = 0;
+  for (; r + 2 < rounds; r += 2) {
+    y.load(row, seg + (r + 1) * step, g1);
+    seg_round<T, VEC>(x, seg + r * step, g1, c, o, s, segs, tag);
+    x.load(row, seg + (r + 2) * step, g1);
+    seg_round<T, VEC>(y, seg + (r + 1) * step, g1, c, o, s, segs, tag);
+  }
+  if (rounds - r == 2) {
+    y.load(row, seg + (r + 1) * step, g1);
+    seg_round<T, VEC>(x, seg + r * step, g1, c, o, s, segs, tag);
+    seg_round<T, VEC>(y, seg + (r + 1) * step, g1, c, o, s, segs, tag);
+  } else {
+    seg_round<T, VEC>(x, seg + r * step, g1, c, o, s, segs, tag);
+  }
+}
+
+// Chunk c of C of a row of G groups: [G c / C, G (c + 1) / C), with both ends rounded down to a
+// multiple of `align` (a power of two; the last chunk ends at G).
+__device__ __forceinline__ void chunk_bounds(int G, int c, int C, int align, int& g0, int& g1) {
+  g0 = (int)((long)G * c / C) & ~(align - 1);
+  g1 = c + 1 == C ? G : (int)((long)G * (c + 1) / C) & ~(align - 1);
+}
+
 // Row-stat group wg = (b * (2K+1) + slot) * C + c. Row slot s <= K is target row s, slot K+1+d
 // is draft row d. Unused rows (s > k_b, d >= k_b) return at once without a read.
 // Publishes stats[b][s][c] = (o, sum) with sum = sum_v 2^(fma(z_v, c32, -o)), and, for target
@@ -622,7 +758,9 @@ __device__ void row_stat_group(const SampleArgs& a, long wg) {
   if (GEN && q.bad) return;
   const int k = q.k;
   const int G = VEC ? V / E : V;
-  const int g0 = (int)((long)G * c / C), g1 = (int)((long)G * (c + 1) / C);
+  const bool bonus = slot == k && a.NS > 0;  // the row of p_k, streamed in segments
+  int g0, g1;
+  chunk_bounds(G, c, C, bonus ? kSegGroups : 1, g0, g1);
   if (GEN && q.greedy) {  // greedy request: argmax partials of target rows 0..k, no draft rows
     if (slot > k) return;
     argmax_chunk<T, VEC>(q.t0 + (size_t)slot * V, g0, g1,
@@ -655,9 +793,15 @@ __device__ void row_stat_group(const SampleArgs& a, long wg) {
               valid ? __float_as_uint(Rows<T, VEC>::at(row, x)) : 0u);
   }
 
-  SoftmaxAcc<E> acc{q.c, -FLT_MAX, 0.0f, 0.0f};
-  stream_groups<T, VEC, kUnroll, false>(row, row, g0, g1, acc);
-  float o = acc.o, s = acc.s0 + acc.s1;
+  float o, s;
+  if (bonus) {
+    stream_segments<T, VEC>(row, g0, g1, q.c, a.seg + (size_t)b * a.NSmax * 2, a.tag, o, s);
+  } else {
+    SoftmaxAcc<E> acc{q.c, -FLT_MAX, 0.0f, 0.0f};
+    stream_groups<T, VEC, kUnroll, false>(row, row, g0, g1, acc);
+    o = acc.o;
+    s = acc.s0 + acc.s1;
+  }
 
   // wave reduce, then across the 4 waves through LDS
   wave_merge_stats(o, s);
@@ -957,6 +1101,60 @@ __device__ int full_row_draw(const T* rt, const DrawParams& w, float c32, int G,
   return y;
 }
 
+// One wave: inverse CDF inside segment t of a bonus row, with the weights its row-stat group
+// summed, 2^(fma(z, c, -o_t)). `target` is on that scale, measured from the segment's start.
+// Returns the first element whose running sum (fp64, element order) exceeds it; if none does
+// (rounding), the last element of the segment with positive weight; -1 if it has none. The
+// segment's kUnroll blocks of 64 groups are scanned in order (fp64 lane sums, a wave prefix sum),
+// and the first lane whose prefix passes the target walks its own elements.
+template <typename T, bool VEC>
+__device__ int segment_find(const T* rt, float c, float ot, int G, int t, double target) {
+  using R = Rows<T, VEC>;
+  constexpr int E = R::E;
+  const int lane = threadIdx.x & 63;
+  typename R::Raw raw[kUnroll];
+#pragma unroll
+  for (int j = 0; j < kUnroll; ++j) {
+    const int g = t * kSegGroups + 64 * j + lane;
+    raw[j] = R::load_cached(rt, g < G ? g : G - 1);
+  }
+  double base = 0.0;
+  int last_pos = -1;
+#pragma unroll
+  for (int j = 0; j < kUnroll; ++j) {
+    const int g = t * kSegGroups + 64 * j + lane;
+    const bool ok = g < G;
+    float f[E], v[E];
+    R::unpack(raw[j], f);
+    double mine = 0.0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      v[e] = ok ? __builtin_amdgcn_exp2f(fmaf(f[e], c, -ot)) : 0.0f;
+      mine += (double)v[e];
+      if (v[e] > 0.0f) last_pos = g * E + e;
+    }
+    const double incl = wave_scan_f64(mine);
+    const double excl = dpp_f64<kDppWaveShr1, 0xf>(incl);
+    const uint64_t hit = __ballot(base + incl > target);
+    if (hit) {
+      const int L = __ffsll((long long)hit) - 1;
+      int cand = INT_MAX;
+      if (lane == L) {
+        double run = base + excl;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          run += (double)v[e];
+          if (cand == INT_MAX && v[e] > 0.0f && run > target) cand = g * E + e;
+        }
+      }
+      cand = (int)lane_u32((uint32_t)cand, L);
+      if (cand != INT_MAX) return cand;
+    }
+    base += lane_f64(incl, 63);
+  }
+  return wave_max_i32(last_pos);
+}
+
 // True in every thread of the group when v is true in any thread: one barrier. `flags` is a
 // kWaves-entry LDS array that no other code touches between the barrier before and after.
 __device__ __forceinline__ bool block_any(bool v, int* flags) {
@@ -969,17 +1167,27 @@ __device__ __forceinline__ bool block_any(bool v, int* flags) {
   return any;
 }
 
-// Normaliser (O, S) of one row from its C staged partials, by one lane, eight LDS reads in
-// flight at a time.
-__device__ __forceinline__ void row_norm(const uint64_t* st, int C, float& O, double& S) {
+// Normaliser (O, S) of one row from its C staged partials st[c * stride], by one lane, eight LDS
+// reads in flight at a time. Partials are staged chunk-major (stride = rows staged), so the lanes
+// of a wave, one row each, read consecutive words: no bank conflicts.
+__device__ __forceinline__ void row_norm(const uint64_t* st, int C, int stride, float& O,
+                                         double& S) {
   O = -FLT_MAX;
   S = 0.0;
   for (int c0 = 0; c0 < C; c0 += 8) {
     uint64_t v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = c0 + u < C ? st[c0 + u] : kEmptyStat;
+    for (int u = 0; u < 8; ++u) v[u] = c0 + u < C ? st[(c0 + u) * stride] : kEmptyStat;
     merge_stats8(O, S, v);
   }
+}
+
+// 2^a for a <= 0 in fp64, to about fp32's relative accuracy: an exact split into the integer
+// part and the fraction, which goes through v_exp_f32 (relative error ~1e-7).
+__device__ __forceinline__ double exp2_split(double a) {
+  const double fl = floor(a);
+  const float fr = (float)(a - fl);  // [0, 1]
+  return ldexp((double)__builtin_amdgcn_exp2f(fr), (int)fmax(fl, -2000.0));
 }
 
 // Greedy request inside a mixed call, by its chunk-0 draw group: waits for the argmax partials of
@@ -1093,8 +1301,8 @@ __device__ void draw_group(const SampleArgs& a, long j) {
 
   // 1. Wait for every partial of the request and the logits at the draft tokens to carry this
   //    call's tag; the words read in the last round are the data. Entries e < nent are
-  //    row-stat partials (staged as offset bits, sum bits), entries nent + i the two logits of
-  //    draft token i.
+  //    row-stat partials, e = row * C + chunk (staged chunk-major as offset bits, sum bits),
+  //    entries nent + i the two logits of draft token i.
   const int nrow = 2 * k + 1, nent = nrow * C;  // nent <= kStageMax by the plan
   const int ntot = nent + k;
   bool late = false;
@@ -1120,7 +1328,7 @@ __device__ void draw_group(const SampleArgs& a, long j) {
     for (int u = 0; u < 4; ++u) {
       const int e = e0 + u * kBlock + (int)threadIdx.x;
       if (e < nent) {
-        stage[e] = ((uint64_t)payload(w0[u]) << 32) | payload(w1[u]);
+        stage[(e % C) * nrow + e / C] = ((uint64_t)payload(w0[u]) << 32) | payload(w1[u]);
       } else if (e < ntot) {
         s_zt[e - nent] = __uint_as_float(payload(w0[u]));
         s_zd[e - nent] = __uint_as_float(payload(w1[u]));
@@ -1139,9 +1347,9 @@ __device__ void draw_group(const SampleArgs& a, long j) {
   float Ot = -FLT_MAX, Od = -FLT_MAX, Ox = -FLT_MAX;
   double St = 0.0, Sd = 0.0, Sx = 0.0;
   if (C <= kLaneRowChunks) {
-    if (lane <= k) row_norm(stage + lane * C, C, Ot, St);
-    if (lane < k) row_norm(stage + (k + 1 + lane) * C, C, Od, Sd);
-    if (k == kMaxK && lane == 0) row_norm(stage + kMaxK * C, C, Ox, Sx);
+    if (lane <= k) row_norm(stage + lane, C, nrow, Ot, St);
+    if (lane < k) row_norm(stage + k + 1 + lane, C, nrow, Od, Sd);
+    if (k == kMaxK && lane == 0) row_norm(stage + kMaxK, C, nrow, Ox, Sx);
   } else {
     int RL = 1;
     while (RL * 16 < C) RL <<= 1;  // C <= kStageMax, so RL <= 128: capped below
@@ -1150,7 +1358,7 @@ __device__ void draw_group(const SampleArgs& a, long j) {
       const int t = t0 + (int)threadIdx.x;
       const int row = t / RL, li = t % RL;
       const bool live = row < nrow;
-      const uint64_t* st = stage + (live ? row : 0) * C;
+      const uint64_t* st = stage + (live ? row : 0);
       float O = -FLT_MAX;
       double S = 0.0;
       for (int c0 = li; c0 < C; c0 += 8 * RL) {
@@ -1158,7 +1366,7 @@ __device__ void draw_group(const SampleArgs& a, long j) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int c = c0 + u * RL;
-          v[u] = c < C ? st[c] : kEmptyStat;
+          v[u] = c < C ? st[c * nrow] : kEmptyStat;
         }
         merge_stats8(O, S, v);
       }
@@ -1184,24 +1392,27 @@ __device__ void draw_group(const SampleArgs& a, long j) {
     }
   }
 
-  // 3. p(x), q(x), the accept decisions and the first rejection n, in every wave.
+  // 3. p(x) = et / St, q(x) = ed / Sd, the accept decisions and the first rejection n, in every
+  //    wave. Slot i is kept when u_i < min(1, p/q), i.e. (u_i < 1) when u_i ed St < et Sd: no
+  //    division on the way to n (the same comparison up to rounding; q = 0 keeps the slot exactly
+  //    when p > 0, a token outside the vocabulary is rejected).
   int n;
   {
-    double p = 0.0, q = 0.0;
+    double et = 0.0, ed = 0.0;
     bool rej = false;
     if (lane < k) {
       if (want_x) {
-        p = exp2((double)s_zt[lane] * (double)c32 - (double)Ot) / St;
-        q = exp2((double)s_zd[lane] * (double)c32 - (double)Od) / Sd;
+        et = exp2_split((double)s_zt[lane] * (double)c32 - (double)Ot);
+        ed = exp2_split((double)s_zd[lane] * (double)c32 - (double)Od);
       }
-      const double t = q > 0.0 ? fmin(1.0, p / q) : (p > 0.0 ? 1.0 : 0.0);
-      rej = !((double)uni < t);
+      rej = !(want_x && (double)uni * ed * St < et * Sd);
     }
     const uint64_t m = __ballot(rej);
     n = m ? (__ffsll((long long)m) - 1) : k;
     if (c2 == 0 && wave == 0 && lane < K) {  // slots k..K-1 get 0
-      a.target_prob[(size_t)b * K + lane] = (float)p;
-      if (a.draft_prob != nullptr) a.draft_prob[(size_t)b * K + lane] = (float)q;
+      a.target_prob[(size_t)b * K + lane] = lane < k ? (float)(et / St) : 0.0f;
+      if (a.draft_prob != nullptr)
+        a.draft_prob[(size_t)b * K + lane] = lane < k ? (float)(ed / Sd) : 0.0f;
     }
   }
 
@@ -1224,6 +1435,59 @@ __device__ void draw_group(const SampleArgs& a, long j) {
   const T* rt = q.t0 + (size_t)n * V;
   const T* rd = resid ? q.d0 + (size_t)n * V : rt;
   const int G = VEC ? V / E : V;
+
+  // 4'. Every draft kept: the token is drawn from p_n (n = k) by the request's first draw group
+  //     alone, from the segment partials of its row-stat groups: await them, scale them to the
+  //     row's offset (exact), pick the segment holding r * Z (every wave, the same answer), and
+  //     wave 0 finds the token inside it. The staged partials are dead by now (every wave has its
+  //     normalisers), so the segment values reuse s_buf: fp64 values, then their fp32 offsets.
+  if (!resid && a.NS > 0) {
+    if (c2 != 0) return;
+    const int NS = a.NS;  // <= kSegMax
+    double* vals = s_buf;
+    float* offs = reinterpret_cast<float*>(s_buf + kSegMax);
+    const uint64_t* sg = a.seg + (size_t)b * a.NSmax * 2;
+    __syncthreads();
+    bool late3 = false;
+    for (int e0 = 0; e0 < NS; e0 += kBlock * 4) {
+      const uint64_t* p[4];
+      bool live[4];
+      uint64_t wo[4], ws[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * kBlock + (int)threadIdx.x;
+        live[u] = e < NS;
+        p[u] = sg + 2 * (live[u] ? e : 0);
+      }
+      late3 = late3 || !await4(p, live, tag, wo, ws);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * kBlock + (int)threadIdx.x;
+        if (e < NS) {
+          const float os = __uint_as_float(payload(wo[u]));
+          const float d = fmaxf(os - w.oT, -2000.0f);  // <= 0: oT is the largest offset
+          vals[e] = ldexp((double)__uint_as_float(payload(ws[u])), (int)d);
+          offs[e] = os;
+        }
+      }
+    }
+    if (block_any(late3, s_late2)) {
+      if (threadIdx.x == 0) a.accepted_len[b] = kTimedOut;
+      return;
+    }
+    const Pick pk = wave_pick(vals, NS, r, 0.0);
+    if (pk.idx < 0) {  // no mass at all (non-finite logits): the tile draw over the whole row
+      const int y = full_row_draw<T, VEC>(rt, w, c32, G, NT, r, s_buf + kStageMax - kChunkTiles);
+      if (threadIdx.x == 0) a.committed[(size_t)b * (K + 1) + n] = y < 0 ? 0 : y;
+      return;
+    }
+    if (wave != 0) return;
+    const float os = offs[pk.idx];
+    const double rel = pk.found ? ldexp(pk.rel, (int)fmaxf(w.oT - os, 0.0f)) : INFINITY;
+    const int y = segment_find<T, VEC>(rt, c32, os, G, pk.idx, rel);
+    if (lane == 0) a.committed[(size_t)b * (K + 1) + n] = y < 0 ? 0 : y;
+    return;
+  }
 
   // 5. Tile sums of this chunk (LDS); wave 0 publishes the chunk total for the other groups of
   //    the request (the same sum that its own pick over the tile sums computes). Tile sums and
@@ -1309,7 +1573,7 @@ __global__ __launch_bounds__(kBlock) void sv_verify_sample(SampleArgs a) {
 // Flattened, mixed calls: the same grid and groups, each request read through its own rows and
 // temperature.
 template <typename T, bool VEC>
-__global__ __launch_bounds__(kBlock) void sv_verify_ragged_kernel(SampleArgs a) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(VEC ? 6 : 1))) void sv_verify_ragged_kernel(SampleArgs a) {
   const long wg = blockIdx.x;
   const long n_stat = (long)a.B * (2 * a.K + 1) * a.C;
   if (wg < n_stat) row_stat_group<T, VEC, true>(a, wg);
@@ -1481,6 +1745,14 @@ bool rows_vectorisable(const void* a, const void* b, int dtype, int V) {
          ((size_t)V * elem_size(dtype)) % 16 == 0;
 }
 
+// Segments of a bonus row (kSegGroups groups of 16-byte vectors or of single elements), or 0 when
+// they do not fit the workspace's slots: then bonus tokens take the tile draw.
+int segments_per_row(int V, int dtype, bool vec, const Plan& p) {
+  const long G = vec ? (long)V * (long)elem_size(dtype) / 16 : (long)V;
+  const long ns = (G + kSegGroups - 1) / kSegGroups;
+  return ns <= p.NSmax ? (int)ns : 0;
+}
+
 template <typename T, bool VEC, bool GEN>
 int launch_sample(const SampleArgs& a, long groups, hipStream_t stream) {
   if (GEN)
@@ -1573,6 +1845,8 @@ int sv_verify_batch(const void* target_logits, const void* draft_logits, int dty
   a.stats = reinterpret_cast<uint64_t*>(ws + L.stats);
   a.gath = reinterpret_cast<uint64_t*>(ws + L.gath);
   a.ctot = reinterpret_cast<uint64_t*>(ws + L.ctot);
+  a.seg = reinterpret_cast<uint64_t*>(ws + L.seg);
+  a.NSmax = p.NSmax;
   a.accepted_len = accepted_len;
   a.committed = committed;
   a.target_prob = target_prob;
@@ -1582,6 +1856,7 @@ int sv_verify_batch(const void* target_logits, const void* draft_logits, int dty
   a.temps = nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool vec = rows_vectorisable(target_logits, draft_logits, dtype, V);
+  a.NS = segments_per_row(V, dtype, vec, p);
   if (dtype == SV_DTYPE_F32)
     return vec ? launch_sample<float, true, false>(a, groups, s)
                : launch_sample<float, false, false>(a, groups, s);
@@ -1641,6 +1916,8 @@ int sv_verify_ragged(const void* target_logits, const void* draft_logits, int dt
   a.stats = reinterpret_cast<uint64_t*>(ws + L.stats);
   a.gath = reinterpret_cast<uint64_t*>(ws + L.gath);
   a.ctot = reinterpret_cast<uint64_t*>(ws + L.ctot);
+  a.seg = reinterpret_cast<uint64_t*>(ws + L.seg);
+  a.NSmax = p.NSmax;
   a.accepted_len = accepted_len;
   a.committed = committed;
   a.target_prob = target_prob;
@@ -1652,6 +1929,7 @@ int sv_verify_ragged(const void* target_logits, const void* draft_logits, int dt
   a.temps = temperature;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool vec = rows_vectorisable(target_logits, a.draft, dtype, V);
+  a.NS = segments_per_row(V, dtype, vec, p);
   if (dtype == SV_DTYPE_F32)
     return vec ? launch_sample<float, true, true>(a, groups, s)
                : launch_sample<float, false, true>(a, groups, s);

@@ -60,6 +60,20 @@ def test_identical_rows_accept_every_draft():
     assert np.all(acc[even] == inp.workload.K)
 
 
+@pytest.mark.parametrize("V,dtype", [
+    (300000, "bf16"),  # 16-byte rows: 147 segments of 2048 logits, the bonus draw reads one
+    (300001, "f32"),   # scalar rows: 1172 segments of 256 logits, more than the workspace keeps,
+                       # so bonus tokens take the tile draw over the whole row
+])
+def test_bonus_draw_segments_and_tile_fallback(V, dtype):
+    inp = generate(BATCHED.replace(name=f"bonus_V{V}_{dtype}", B=4, K=2, V=V, dtype=dtype,
+                                   seed=37 + V % 7))
+    _check(inp)
+    acc, _, _, _ = run_sample(inp.target, inp.draft, inp.tokens, inp.uniforms, inp.residual,
+                              inp.workload.temperature)
+    assert np.all(acc[0::2] == 2)  # identical draft rows: every draft kept, a bonus token drawn
+
+
 def test_zero_drafts_and_out_of_range_tokens():
     w = TINY.replace(B=6, K=5, V=3000, seed=41)
     inp = generate(w)
