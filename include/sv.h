@@ -199,10 +199,19 @@ int sv_schedule_prefix(const float* confidence, int B, int K, const float* step_
  *  draft_tokens  [B, K] int32 out; draft_logits [B, K, V] dtype out or NULL (bf16 rounds to
  *                nearest even)
  *  workspace     sv_markov_workspace_bytes(B, V) bytes, 256-byte aligned, device, owned by the
- *                caller, no clearing needed. It is left holding per-tile argmaxes, not tagged
- *                words: zero it before handing the same memory to sv_verify_*.
- * 2K launches on `stream`. Returns SV_OK, SV_ERR_INVALID_ARG, SV_ERR_WORKSPACE,
- * SV_ERR_UNSUPPORTED or SV_ERR_HIP; nothing is launched unless SV_OK.
+ *                caller, no clearing needed between calls of this function. It is left holding
+ *                words stamped with this function's own call numbers (or per-tile argmaxes):
+ *                zero it before handing the same memory to sv_verify_*.
+ * With B <= 64 and R <= 256, and when every vocabulary tile fits the registers of a resident
+ * work-group (at most five tiles of 64 entries each; V = 151936 on 256 compute units fits), one
+ * launch does all K positions: each work-group keeps the right-factor rows of its tiles in
+ * registers from the first position to the last, and the work-groups hand the positions' tokens
+ * to each other through tagged words in the workspace (waits bounded at about 2 s; a token that
+ * could not be formed, which needs all of the launch's work-groups not to be resident at once,
+ * is reported as -2 at that position and after). Otherwise 2K launches (a bias-and-argmax
+ * launch and a finishing launch per position). All on `stream`. Returns SV_OK,
+ * SV_ERR_INVALID_ARG, SV_ERR_WORKSPACE, SV_ERR_UNSUPPORTED or SV_ERR_HIP; nothing is launched
+ * unless SV_OK.
  */
 size_t sv_markov_workspace_bytes(int B, int V);
 int sv_markov_draft(const void* base_logits, int dtype, int B, int K, int V,

@@ -17,6 +17,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include <float.h>
 #include <limits.h>
 #include <math.h>
@@ -289,20 +291,25 @@ __device__ __forceinline__ void stage_tokens(int (&p)[kReqBlock / 8],
 }
 
 // Stages the left-factor rows of the block's previous tokens into sa (rank words past R and
-// rows without a token are zero), then waits for the whole work-group.
+// rows without a token are zero), then waits for the whole work-group. NB rows per batch of
+// loads in flight (fewer: fewer registers).
+template <int NB = kReqBlock / 8>
 __device__ __forceinline__ void stage_rows(uint16_t (*sa)[kARow], const int (&p)[kReqBlock / 8],
                                            const uint16_t* __restrict__ left, int R) {
   const int sw = threadIdx.x & 31, nw = R / 8;  // 16-byte words per row
   const int wd = sw < nw ? sw : nw - 1;
-  v4u32 aw[kReqBlock / 8];
 #pragma unroll
-  for (int u = 0; u < kReqBlock / 8; ++u)
-    aw[u] = reinterpret_cast<const v4u32*>(left + (size_t)(p[u] >= 0 ? p[u] : 0) * R)[wd];
+  for (int u0 = 0; u0 < kReqBlock / 8; u0 += NB) {
+    v4u32 aw[NB];
 #pragma unroll
-  for (int u = 0; u < kReqBlock / 8; ++u) {
-    const bool ok = p[u] >= 0 && sw < nw;
-    *reinterpret_cast<v4u32*>(&sa[(threadIdx.x >> 5) + 8 * u][8 * sw]) =
-        ok ? aw[u] : v4u32{0u, 0u, 0u, 0u};
+    for (int u = 0; u < NB; ++u)
+      aw[u] = reinterpret_cast<const v4u32*>(left + (size_t)(p[u0 + u] >= 0 ? p[u0 + u] : 0) * R)[wd];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const bool ok = p[u0 + u] >= 0 && sw < nw;
+      *reinterpret_cast<v4u32*>(&sa[(threadIdx.x >> 5) + 8 * (u0 + u)][8 * sw]) =
+          ok ? aw[u] : v4u32{0u, 0u, 0u, 0u};
+    }
   }
   __syncthreads();
 }
@@ -520,6 +527,298 @@ __global__ __launch_bounds__(kThreads) void markov_finish(const uint64_t* __rest
   }
 }
 
+
+// ---------------------------------------------------------------------------------------------
+// All K positions in one launch, for up to 64 requests at ranks up to 256. Work-group w owns
+// vocabulary tiles [w per, (w + 1) per) (per <= kResItems) for every position and holds their
+// right-factor rows in registers from the first position to the last, so that a position moves
+// only its base and corrected logits (and the left rows of the previous tokens). Between two
+// positions the work-groups hand off through tagged words (the call's tag plus the position in
+// the upper half, the payload in the lower; agent-scope atomic stores and loads):
+//   * each work-group publishes, per request, the argmax (value, index) over its tiles;
+//   * work-group b (b < B) waits for those of request b, reduces them (lowest index on ties) to
+//     the position's token, writes it and publishes it;
+//   * every work-group waits for the B tokens, gathers their left rows, and goes on.
+// Every wait depends only on work-groups that are resident at the same time (the grid is at
+// most one work-group per slot) and is bounded: after kResSpin polls it gives up, and the
+// request's token at that position and after is reported as -2.
+constexpr int kResItems = 5;       // vocabulary tiles per work-group, factor rows in registers
+constexpr int kResSpin = 1 << 21;  // polls before a wait gives up
+constexpr int32_t kResFailed = -2;
+
+struct ResArgs {
+  int B, K, V, R, ns, ntile, per, nwg;
+  const uint16_t* left;
+  const uint16_t* right;
+  const int32_t* anchor;
+  int32_t* tokens;  // [B][K]
+  uint64_t* part;   // [B][nwg][2] tagged (value bits, index) of each work-group's tiles
+  uint64_t* tok;    // [B] tagged token of the latest position
+  uint32_t tag;     // position k publishes with tag + k (the host steps tags by 64)
+};
+
+__device__ __forceinline__ void res_publish(uint64_t* p, uint32_t tag, uint32_t payload) {
+  __hip_atomic_store(p, ((uint64_t)tag << 32) | payload, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t res_fetch(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Polls *p until its tag is `tag` (at most kResSpin polls). Returns the payload, or fails.
+__device__ __forceinline__ bool res_await(const uint64_t* p, uint32_t tag, uint32_t& payload) {
+  uint64_t v = res_fetch(p);
+  for (int left = kResSpin; (uint32_t)(v >> 32) != tag; --left) {
+    if (left == 0) return false;
+    __builtin_amdgcn_s_sleep(2);
+    v = res_fetch(p);
+  }
+  payload = (uint32_t)v;
+  return true;
+}
+
+// A barrier for LDS traffic only: this wave's LDS accesses complete, then the work-group meets.
+// (__syncthreads would also wait for every global load and store in flight, among them the
+// ring's loads.) The empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One tile of the work-group at position k: contract the staged left rows with the tile's factor
+// words f (registers), add the base logits bv, write the corrected logits and fold the tile's
+// per-request argmax into (run, run_i) (every thread of a row holds the row's).
+template <typename T, bool VEC, bool FULL>
+__device__ __forceinline__ void res_tile(const ResArgs& a, T* __restrict__ out,
+                                         uint16_t (*sa)[kARow], float (*sz)[kZRow], int k,
+                                         int tile, const v4u32 (&f)[kSteps], const Base<T>& bv,
+                                         float& run, int& run_i) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float4_t acc[4] = {{}, {}, {}, {}};
+#pragma unroll
+  for (int t = 0; t < kSteps; ++t) {
+    if (FULL || t < a.ns) {  // uniform
+      const bool inside = FULL || 4 * t + (lane >> 4) < a.R / 8;
+      const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, inside ? f[t] : v4u32{0u, 0u, 0u, 0u});
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const v4u32 x =
+            *reinterpret_cast<const v4u32*>(&sa[rb * 16 + (lane & 15)][32 * t + 8 * (lane >> 4)]);
+        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x), bfr,
+                                                          acc[rb], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      sz[rb * 16 + 4 * (lane >> 4) + i][wave * 16 + (lane & 15)] = acc[rb][i];
+  lds_barrier();
+  const int m = tid >> 2, q = tid & 3;
+  const int v0 = tile * kStreamTile + 16 * q;
+  if (16 * wave < a.B) {  // uniform over the wave
+    float z[16];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const float4 acc4 = *reinterpret_cast<const float4*>(&sz[m][16 * q + 4 * x]);
+      z[4 * x] = logit_at<T>(bv, 4 * x) + acc4.x;
+      z[4 * x + 1] = logit_at<T>(bv, 4 * x + 1) + acc4.y;
+      z[4 * x + 2] = logit_at<T>(bv, 4 * x + 2) + acc4.z;
+      z[4 * x + 3] = logit_at<T>(bv, 4 * x + 3) + acc4.w;
+    }
+    const bool row_ok = m < a.B;
+    const int ncol = a.V - v0;
+    float best = -INFINITY;
+    int e_best = -1;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const bool take = row_ok && e < ncol && z[e] > best;
+      best = take ? z[e] : best;
+      e_best = take ? e : e_best;
+    }
+    int bi = e_best < 0 ? INT_MAX : v0 + e_best;
+    if (out != nullptr && row_ok) {
+      T* orow = out + ((size_t)m * a.K + k) * (size_t)a.V + v0;
+      if constexpr (VEC) {
+        constexpr int kVec = Base<T>::kVec;
+#pragma unroll
+        for (int w = 0; w < Base<T>::kWords; ++w) {
+          if (w * kVec < ncol) {
+            if constexpr (sizeof(T) == 4) {
+              *reinterpret_cast<float4*>(orow + 4 * w) =
+                  make_float4(z[4 * w], z[4 * w + 1], z[4 * w + 2], z[4 * w + 3]);
+            } else {
+              uint32_t r[4];
+#pragma unroll
+              for (int x = 0; x < 4; ++x)
+                r[x] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)z[8 * w + 2 * x],
+                                                             (__bf16)z[8 * w + 2 * x + 1]});
+              *reinterpret_cast<v4u32*>(orow + 8 * w) = v4u32{r[0], r[1], r[2], r[3]};
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (e < ncol) Logit<T>::put(orow + e, z[e]);
+      }
+    }
+#pragma unroll
+    for (int sh = 1; sh <= 2; sh <<= 1) {
+      const float b2 = __shfl_xor(best, sh);
+      const int i2 = __shfl_xor(bi, sh);
+      if (better(b2, i2, best, bi)) {
+        best = b2;
+        bi = i2;
+      }
+    }
+    if (better(best, bi, run, run_i)) {
+      run = best;
+      run_i = bi;
+    }
+  }
+  lds_barrier();  // sz is rewritten by the next tile
+}
+
+template <typename T, bool VEC, bool FULL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void
+markov_resident(const T* __restrict__ base, T* __restrict__ out, ResArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sa[kReqBlock][kARow];
+  __shared__ __attribute__((aligned(16))) float sz[kReqBlock][kZRow];
+  __shared__ int s_tok[kReqBlock];
+  __shared__ float s_best[kWaves];
+  __shared__ int s_bi[kWaves], s_late[kWaves];
+  const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = w * a.per;
+  const int nit = a.ntile - t0 < a.per ? (a.ntile - t0 > 0 ? a.ntile - t0 : 0) : a.per;
+  v4u32 f[kResItems][kSteps];
+#pragma unroll
+  for (int i = 0; i < kResItems; ++i) {
+    const int tile = t0 + i < a.ntile ? t0 + i : a.ntile - 1;
+    load_factor(f[i], a.right, a.V, a.R, tile);
+  }
+  for (int k = 0; k < a.K; ++k) {
+    const uint32_t tg = a.tag + (uint32_t)k;
+    Base<T> bb[2];
+    load_base<T, VEC>(bb[0], base, a.B, a.K, a.V, k, t0 < a.ntile ? t0 : a.ntile - 1, 0);
+    // 1. the previous tokens (the anchor at k = 0)
+    if (tid < kReqBlock) {
+      int x = -1;
+      if (tid < a.B) {
+        if (k == 0) {
+          x = a.anchor != nullptr ? a.anchor[tid] : -1;
+        } else {
+          uint32_t pl;
+          x = res_await(a.tok + tid, tg - 1u, pl) ? (int)pl : kResFailed;
+        }
+      }
+      s_tok[tid] = x;
+    }
+    lds_barrier();
+    int p[kReqBlock / 8];
+#pragma unroll
+    for (int u = 0; u < kReqBlock / 8; ++u) {
+      const int x = s_tok[(tid >> 5) + 8 * u];
+      p[u] = (x >= 0 && x < a.V) ? x : -1;
+    }
+    stage_rows(sa, p, a.left, a.R);
+    // 2. the work-group's tiles, the base logits of the next one in flight
+    float run = -INFINITY;
+    int run_i = INT_MAX;
+#pragma unroll
+    for (int i = 0; i < kResItems; ++i) {
+      if (i < nit) {  // uniform
+        if (i + 1 < nit)
+          load_base<T, VEC>(bb[(i + 1) & 1], base, a.B, a.K, a.V, k, t0 + i + 1, 0);
+        res_tile<T, VEC, FULL>(a, out, sa, sz, k, t0 + i, f[i], bb[i & 1], run, run_i);
+      }
+    }
+    // 3. this work-group's argmax of each request
+    if ((tid & 3) == 0 && (tid >> 2) < a.B) {
+      uint64_t* pp = a.part + ((size_t)(tid >> 2) * a.nwg + w) * 2;
+      res_publish(pp, tg, __float_as_uint(run));
+      res_publish(pp + 1, tg, (uint32_t)run_i);
+    }
+    // 4. work-group b < B: the token of request b
+    if (w < a.B) {
+      const int b = w;
+      float best = -INFINITY;
+      int bi = INT_MAX;
+      bool late = false;
+      for (int j0 = 0; j0 < a.nwg; j0 += 2 * kThreads) {  // two partials per thread in flight
+        const uint64_t* pp[2];
+        uint64_t v[4];
+        bool live[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int j = j0 + u * kThreads + tid;
+          live[u] = j < a.nwg;
+          pp[u] = a.part + ((size_t)b * a.nwg + (live[u] ? j : 0)) * 2;
+          v[2 * u] = live[u] ? res_fetch(pp[u]) : (uint64_t)tg << 32;
+          v[2 * u + 1] = live[u] ? res_fetch(pp[u] + 1) : (uint64_t)tg << 32;
+        }
+        for (int left = kResSpin;; --left) {
+          bool all = true;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) all = all && (uint32_t)(v[x] >> 32) == tg;
+          if (all) break;
+          if (left == 0) {
+            late = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            if ((uint32_t)(v[x] >> 32) != tg) v[x] = res_fetch(pp[x >> 1] + (x & 1));
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          if (live[u]) {
+            const float z = __uint_as_float((uint32_t)v[2 * u]);
+            const int i = (int)(uint32_t)v[2 * u + 1];
+            if (better(z, i, best, bi)) {
+              best = z;
+              bi = i;
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int sh = 32; sh >= 1; sh >>= 1) {
+        const float b2 = __shfl_xor(best, sh);
+        const int i2 = __shfl_xor(bi, sh);
+        if (better(b2, i2, best, bi)) {
+          best = b2;
+          bi = i2;
+        }
+      }
+      const bool wave_late = __ballot(late) != 0;
+      if (lane == 0) {
+        s_best[wave] = best;
+        s_bi[wave] = bi;
+        s_late[wave] = wave_late;
+      }
+      lds_barrier();
+      if (tid == 0) {
+        bool any_late = false;
+        for (int v = 0; v < kWaves; ++v) {
+          any_late = any_late || s_late[v] != 0;
+          if (better(s_best[v], s_bi[v], best, bi)) {
+            best = s_best[v];
+            bi = s_bi[v];
+          }
+        }
+        const bool failed = any_late || s_tok[b] == kResFailed;
+        const int token = failed ? kResFailed : (bi == INT_MAX ? 0 : bi);
+        a.tokens[(size_t)b * a.K + k] = token;
+        res_publish(a.tok + b, tg, (uint32_t)token);
+      }
+    }
+    lds_barrier();  // s_tok, s_best are rewritten at the next position
+  }
+}
+
 bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
 // Compute units of the current device (cached per device).
@@ -537,6 +836,65 @@ int cu_count() {
   return cached[dev];
 }
 
+// Call tags of the one-launch form: steps of 64, so that tag + k (k < 64) never meets another
+// call's; 0 (a fresh workspace) is never one.
+std::atomic<uint32_t> g_res_tag{0};
+
+uint32_t next_res_tag() {
+  uint32_t t;
+  do {
+    t = g_res_tag.fetch_add(64u, std::memory_order_relaxed) + 64u;
+  } while (t == 0);
+  return t;
+}
+
+// The one-launch form (markov_resident) when it applies: up to 64 requests, ranks up to 256,
+// every tile of the vocabulary in a resident work-group's registers (at most kResItems each),
+// and at least one work-group per request. Returns false when it does not apply.
+template <typename T>
+bool launch_resident(const void* base, void* out, int B, int K, int V, const uint16_t* left,
+                     const uint16_t* right, int R, const int32_t* anchor, int32_t* tokens,
+                     uint64_t* ws, bool vec_rows, hipStream_t s) {
+  if (B > kReqBlock || R > kRankChunk) return false;
+  const int ntile = (V + kStreamTile - 1) / kStreamTile;
+  const bool full = R == kRankChunk;
+  const void* fn =
+      full ? (vec_rows ? reinterpret_cast<const void*>(&markov_resident<T, true, true>)
+                       : reinterpret_cast<const void*>(&markov_resident<T, false, true>))
+           : (vec_rows ? reinterpret_cast<const void*>(&markov_resident<T, true, false>)
+                       : reinterpret_cast<const void*>(&markov_resident<T, false, false>));
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess ||
+      per_cu < 1)
+    return false;
+  const int slots = per_cu * cu_count();
+  const int per = (ntile + slots - 1) / slots;
+  if (per > kResItems) return false;
+  int nwg = (ntile + per - 1) / per;
+  nwg = nwg < B ? B : nwg;
+  if (nwg > slots) return false;
+  ResArgs a;
+  a.B = B;
+  a.K = K;
+  a.V = V;
+  a.R = R;
+  a.ns = (R + 31) / 32;
+  a.ntile = ntile;
+  a.per = per;
+  a.nwg = nwg;
+  a.left = left;
+  a.right = right;
+  a.anchor = anchor;
+  a.tokens = tokens;
+  a.part = ws;                         // [B][nwg][2]
+  a.tok = ws + (size_t)2 * B * nwg;    // [B]
+  a.tag = next_res_tag();
+  hipLaunchKernelGGL(
+      reinterpret_cast<void (*)(const T*, T*, ResArgs)>(const_cast<void*>(fn)), dim3(nwg),
+      dim3(kThreads), 0, s, static_cast<const T*>(base), static_cast<T*>(out), a);
+  return true;
+}
+
 template <typename T>
 int launch_all(const void* base, void* out, int B, int K, int V, const uint16_t* left,
                const uint16_t* right, int R, const int32_t* anchor, int32_t* tokens,
@@ -547,6 +905,11 @@ int launch_all(const void* base, void* out, int B, int K, int V, const uint16_t*
   const int n = ntile * nrb;
   const int groups = 8 * ((n + 7) / 8);
   const bool vec_rows = aligned16(base) && aligned16(out) && ((size_t)V * sizeof(T)) % 16 == 0;
+  if (launch_resident<T>(base, out, B, K, V, left, right, R, anchor, tokens, part, vec_rows, s)) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return sv_internal_fail(SV_ERR_HIP, hipGetErrorString(e));
+    return SV_OK;
+  }
   // persistent form: as many work-groups as are resident at once, each a contiguous run of
   // equally many items
   const bool full = R == kRankChunk;
@@ -586,7 +949,11 @@ int launch_all(const void* base, void* out, int B, int K, int V, const uint16_t*
 
 extern "C" size_t sv_markov_workspace_bytes(int B, int V) {
   if (B < 1 || V < 1) return 0;
-  return (size_t)B * ((V + kStreamTile - 1) / kStreamTile) * 8;  // tile partials, either form
+  const size_t ntile = (V + kStreamTile - 1) / kStreamTile;
+  const size_t per_position = (size_t)B * ntile * 8;  // tile partials of the per-position form
+  // one-launch form: [B][nwg][2] tagged partials (nwg <= max(ntile, B)) and [B] tagged tokens
+  const size_t one_launch = (size_t)B * (ntile > (size_t)B ? ntile : (size_t)B) * 16 + (size_t)B * 8;
+  return per_position > one_launch ? per_position : one_launch;
 }
 
 extern "C" int sv_markov_draft(const void* base_logits, int dtype, int B, int K, int V,

@@ -119,6 +119,18 @@ def test_markov_parity(dtype, B, K, V, R):
     check_batch(f"{dtype} B{B} K{K} V{V} R{R}", base, dtype, left, right, anchor)
 
 
+def test_markov_sixty_four_positions():
+    """K = 64: every hand-off between positions of the one-launch form, 64 of them in one call,
+    and a second call on the same workspace (fresh call stamps)."""
+    B, K, V, R = 5, 64, 600, 32
+    base = workloads.markov_base(B, K, V, "bf16", seed=81)
+    left, right = workloads.markov_factors(V, R, seed=82)
+    anchor = np.arange(B, dtype=np.int32) * 7
+    tok1, z1 = check_batch("K64", base, "bf16", left, right, anchor)
+    tok2, z2 = run(base, left, right, anchor)
+    assert np.array_equal(tok1, tok2) and np.array_equal(z1, z2)
+
+
 def test_markov_no_anchor_and_no_logits():
     B, K, V, R = 9, 4, 777, 64
     base = workloads.markov_base(B, K, V, "f32", seed=21)
