@@ -375,7 +375,17 @@ __global__ __launch_bounds__(kThreads) void topk_chunk(const T* __restrict__ bas
   const float f0 = key_value(t0);
   if (t0 != 0u) {
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e) n_ge += raw_value<T>(raw, e) >= f0;  // NaN: false
+    for (int w = 0; w < kPerThread * (int)sizeof(T) / 4; ++w) {
+      uint32_t word[1] = {raw[w]};
+      asm volatile("" : "+v"(word[0]));  // unpack afresh here: no unpacked copies stay live
+      constexpr int kPer = 4 / (int)sizeof(T);
+#pragma unroll
+      for (int x = 0; x < kPer; ++x) {
+        const float f = sizeof(T) == 4 ? __uint_as_float(word[0])
+                                       : __uint_as_float(x ? (word[0] & 0xffff0000u) : (word[0] << 16));
+        n_ge += f >= f0;  // NaN: false
+      }
+    }
   }
   const int incl = block_scan(n_ge, sh.red);
   if (tid == kThreads - 1) sh.n_all = incl;
@@ -386,9 +396,16 @@ __global__ __launch_bounds__(kThreads) void topk_chunk(const T* __restrict__ bas
   if (!fast) return;  // uniform: ties at the bound, or too few numbers
   int at = incl - n_ge;
 #pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
-    const float f = raw_value<T>(raw, e);
-    if (f >= f0) sh.list[at++] = ((uint64_t)order_key(f) << 32) | (uint32_t)(v0 + e);
+  for (int w = 0; w < kPerThread * (int)sizeof(T) / 4; ++w) {
+    uint32_t word = raw[w];
+    asm volatile("" : "+v"(word));
+    constexpr int kPer = 4 / (int)sizeof(T);
+#pragma unroll
+    for (int x = 0; x < kPer; ++x) {
+      const float f = sizeof(T) == 4 ? __uint_as_float(word)
+                                     : __uint_as_float(x ? (word & 0xffff0000u) : (word << 16));
+      if (f >= f0) sh.list[at++] = ((uint64_t)order_key(f) << 32) | (uint32_t)(v0 + kPer * w + x);
+    }
   }
   __syncthreads();
   uint64_t* dst = out + ((size_t)r * nchunk + c) * kMaxCand;
