@@ -332,3 +332,15 @@ def markov_base(B: int, K: int, V: int, dtype: str = "bf16", seed: int = 1009) -
     lead = rng.integers(0, V, size=(B, K))
     np.put_along_axis(z, lead[..., None], np.take_along_axis(z, lead[..., None], 2) + 6.0, 2)
     return _stored(z, dtype)
+
+
+def markov_sampling(B: int, K: int, seed: int = 1010, greedy_share: float = 0.0,
+                    temperatures=(1.0,)):
+    """Per-request temperatures [B] float32 and per-position uniforms [B, K] float32 in [0, 1)
+    for the sampled Markov head: each request takes one of `temperatures` (1.0 is the pages'
+    evaluation setting), and a `greedy_share` of the requests temperature 0 (greedy)."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, B, K]))
+    tau = rng.choice(np.asarray(temperatures, dtype=np.float32), size=B).astype(np.float32)
+    tau[rng.random(B) < greedy_share] = 0.0
+    u = rng.random((B, K), dtype=np.float32)
+    return tau, u
