@@ -219,6 +219,40 @@ int sv_markov_draft(const void* base_logits, int dtype, int B, int K, int V,
                     const int32_t* anchor, int32_t* draft_tokens, void* draft_logits,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Sampled Markov-head drafting (DSpark paper review, 4.1 Semi-autoregressive generation: the head
+ * samples each position's token and biases the next position with the sample; "Accelerating
+ * Large-Model Inference ...", section 3, evaluation at temperature 1.0). The correction is that
+ * of sv_markov_draft; the token of position k of request b (tau = temperature[b]):
+ *   tau == 0: argmax_v corrected[b][k][v], exactly as sv_markov_draft;
+ *   tau >= log2(e) / 2^21 and finite: a draw from softmax(d[b][k] / tau), d = the draft_logits
+ *     row as stored (bf16: the rounded values, so the draw follows the q row a verifier reads),
+ *     by inverse CDF in ascending vocabulary order with u = uniforms[b][k] clamped to [0, 1]
+ *     (NaN as 0): the first v whose running mass passes u * (row mass); entries that are NaN or
+ *     -inf have no mass; when the row's largest value is +inf only its +inf entries have mass;
+ *     a row without mass gives token 0;
+ *   any other tau: token -3 at every position (its later positions then get no bias).
+ * The drawn token is prev for position k + 1.
+ *
+ *  base_logits, left_factor, right_factor, R, anchor, draft_tokens as sv_markov_draft
+ *  temperature   [B] float, device
+ *  uniforms      [B, K] float, device
+ *  draft_logits  [B, K, V] dtype out, device, required (the draws read the stored rows back)
+ *  workspace     sv_markov_workspace_bytes(B, V) bytes, as sv_markov_draft
+ * The one-launch form of sv_markov_draft only (R <= 256 and every vocabulary tile in a resident
+ * work-group), one launch per block of 64 requests, all on `stream`. Within a launch the
+ * work-groups also hand off each draw: the request's finishing work-group finds which
+ * work-group's share of the distribution holds the target, and that work-group finds the token
+ * in the entries it wrote. Waits are bounded as in sv_markov_draft (token -2 when one gives up).
+ * Returns SV_OK, SV_ERR_INVALID_ARG, SV_ERR_WORKSPACE, SV_ERR_UNSUPPORTED (R > 256, or the
+ * vocabulary does not fit the resident work-groups) or SV_ERR_HIP; nothing is launched for
+ * SV_ERR_INVALID_ARG, SV_ERR_WORKSPACE or R > 256.
+ */
+int sv_markov_draft_sampled(const void* base_logits, int dtype, int B, int K, int V,
+                            const uint16_t* left_factor, const uint16_t* right_factor, int R,
+                            const int32_t* anchor, const float* temperature,
+                            const float* uniforms, int32_t* draft_tokens, void* draft_logits,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* Top-K Markov drafting ("Bringing DSpark to vLLM Metal", Making the draft cheaper): per draft
  * position the candidates are the kc largest base logits (NaN below every number, ties to the
  * lower index), and the Markov correction of sv_markov_draft is applied to those rows only:

@@ -69,6 +69,9 @@ def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
         lib.sv_markov_draft.argtypes = [vp, i32, i32, i32, i32, vp, vp, i32, vp, vp, vp, vp, sz,
                                         vp]
         lib.sv_markov_draft.restype = i32
+        lib.sv_markov_draft_sampled.argtypes = [vp, i32, i32, i32, i32, vp, vp, i32, vp, vp, vp,
+                                                vp, vp, vp, sz, vp]
+        lib.sv_markov_draft_sampled.restype = i32
         lib.sv_markov_topk_workspace_bytes.argtypes = [i32, i32, i32]
         lib.sv_markov_topk_workspace_bytes.restype = sz
         lib.sv_markov_topk.argtypes = [vp, i32, i32, i32, i32, vp, vp, i32, i32, vp, vp, vp, vp,
@@ -326,6 +329,42 @@ def sv_markov_draft(base: torch.Tensor, left_factor: torch.Tensor, right_factor:
     _check(lib.sv_markov_draft(_ptr(base), _dtype_code(base), B, K, V, _ptr(left_factor),
                                _ptr(right_factor), R, _ptr(anchor), _ptr(tokens), _ptr(out),
                                _ptr(ws), ws.numel(), stream))
+    return tokens, out
+
+
+def sv_markov_draft_sampled(base: torch.Tensor, left_factor: torch.Tensor,
+                            right_factor: torch.Tensor, temperature: torch.Tensor,
+                            uniforms: torch.Tensor, anchor: Optional[torch.Tensor] = None):
+    """Sampled Markov-head drafting on the tensors' GPU (see sv_markov_draft_sampled in
+    include/sv.h). base [B, K, V] float32 or bfloat16; left_factor, right_factor [V, R]
+    bfloat16; temperature [B] float32 (0: argmax); uniforms [B, K] float32; anchor [B] int32 or
+    None. Returns (tokens [B, K] int32, draft logits [B, K, V] of base's dtype)."""
+    lib = load_library()
+    if base.dim() != 3:
+        raise ValueError("base must be [B, K, V]")
+    B, K, V = base.shape
+    dev = base.device
+    if dev.type != "cuda":
+        raise ValueError("base must be a GPU tensor")
+    _need(base, "base", base.dtype, (B, K, V), dev)
+    if left_factor.dim() != 2:
+        raise ValueError("left_factor must be [V, R]")
+    R = left_factor.shape[1]
+    _need(left_factor, "left_factor", torch.bfloat16, (V, R), dev)
+    _need(right_factor, "right_factor", torch.bfloat16, (V, R), dev)
+    _need(temperature, "temperature", torch.float32, (B,), dev)
+    _need(uniforms, "uniforms", torch.float32, (B, K), dev)
+    if anchor is not None:
+        _need(anchor, "anchor", torch.int32, (B,), dev)
+    tokens = torch.empty(B, K, dtype=torch.int32, device=dev)
+    out = torch.empty_like(base)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    nbytes = int(lib.sv_markov_workspace_bytes(B, V))
+    ws = _workspace(dev, stream, nbytes, "markov")
+    _check(lib.sv_markov_draft_sampled(_ptr(base), _dtype_code(base), B, K, V, _ptr(left_factor),
+                                       _ptr(right_factor), R, _ptr(anchor), _ptr(temperature),
+                                       _ptr(uniforms), _ptr(tokens), _ptr(out), _ptr(ws),
+                                       ws.numel(), stream))
     return tokens, out
 
 

@@ -49,6 +49,7 @@ template <>
 struct Logit<float> {
   __device__ static float get(float x) { return x; }
   __device__ static void put(float* p, float x) { *p = x; }
+  __device__ static float stored(float x) { return x; }  // the value put() leaves
 };
 template <>
 struct Logit<uint16_t> {
@@ -57,6 +58,8 @@ struct Logit<uint16_t> {
     const uint32_t b = __float_as_uint(x);
     *p = (x != x) ? (uint16_t)0x7FC0 : (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
   }
+  // the value put() (and the vector stores' conversion) leaves, as a float
+  __device__ static float stored(float x) { return (float)(__bf16)x; }
 };
 
 __device__ __forceinline__ short4_t lo4(v4u32 v) {
@@ -555,7 +558,24 @@ struct ResArgs {
   uint64_t* part;   // [B][nwg][2] tagged (value bits, index) of each work-group's tiles
   uint64_t* tok;    // [B] tagged token of the latest position
   uint32_t tag;     // position k publishes with tag + k (the host steps tags by 64)
+  // sampled form only
+  const float* tau;  // [B] temperatures: 0 argmax, >= kTauMin and finite a draw, else invalid
+  const float* uni;  // [B][K] one uniform per position
+  uint64_t* dec;     // [B][2] tagged draw decision: owning work-group, target in its scale
 };
+
+constexpr double kLog2e = 1.4426950408889634074;
+constexpr double kTauMin = kLog2e / 2097152.0;  // smallest sampling temperature: c <= 2^21
+constexpr int32_t kInvalid = -3;                 // tokens of a request whose temperature is invalid
+constexpr uint32_t kNoOwner = 0xFFFFFFFFu;       // decision payload: no work-group draws
+constexpr int kDecideLoads = 4;                  // partials per thread of a draw decision
+
+// Weight of a stored logit y in a draw at inverse temperature c (log2 e / tau), relative to the
+// offset m (a value >= every y it is applied to): 2^((y - m) c); NaN and -inf weigh 0, and y == m
+// weighs 1 (also when both are +inf).
+__device__ __forceinline__ float draw_weight(float y, float m, float c) {
+  return y > -INFINITY ? __builtin_amdgcn_exp2f(y == m ? 0.0f : (y - m) * c) : 0.0f;
+}
 
 __device__ __forceinline__ void res_publish(uint64_t* p, uint32_t tag, uint32_t payload) {
   __hip_atomic_store(p, ((uint64_t)tag << 32) | payload, __ATOMIC_RELAXED,
@@ -588,11 +608,11 @@ __device__ __forceinline__ void lds_barrier() {
 // One tile of the work-group at position k: contract the staged left rows with the tile's factor
 // words f (registers), add the base logits bv, write the corrected logits and fold the tile's
 // per-request argmax into (run, run_i) (every thread of a row holds the row's).
-template <typename T, bool VEC, bool FULL>
+template <typename T, bool VEC, bool FULL, bool SAMPLED>
 __device__ __forceinline__ void res_tile(const ResArgs& a, T* __restrict__ out,
                                          uint16_t (*sa)[kARow], float (*sz)[kZRow], int k,
                                          int tile, const v4u32 (&f)[kSteps], const Base<T>& bv,
-                                         float& run, int& run_i) {
+                                         float& run, int& run_i, float c, float& sm, float& ss) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float4_t acc[4] = {{}, {}, {}, {}};
 #pragma unroll
@@ -677,11 +697,235 @@ __device__ __forceinline__ void res_tile(const ResArgs& a, T* __restrict__ out,
       run = best;
       run_i = bi;
     }
+    if constexpr (SAMPLED) {
+      // the row's mass over the work-group's tiles, online: sm the largest stored value so far,
+      // ss the sum of draw_weight(y, sm, c) (each thread of a row holds the row's)
+      float y[16];
+      float tm = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        y[e] = Logit<T>::stored(z[e]);
+        y[e] = (row_ok && e < ncol) ? y[e] : -INFINITY;
+        tm = y[e] > tm ? y[e] : tm;
+      }
+      tm = fmaxf(tm, __shfl_xor(tm, 1));
+      tm = fmaxf(tm, __shfl_xor(tm, 2));
+      const float nm = fmaxf(sm, tm);
+      float ts = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) ts += draw_weight(y[e], nm, c);
+      ts += __shfl_xor(ts, 1);
+      ts += __shfl_xor(ts, 2);
+      ss = ss * (sm == nm ? 1.0f : __builtin_amdgcn_exp2f((sm - nm) * c)) + ts;
+      sm = nm;
+    }
   }
   lds_barrier();  // sz is rewritten by the next tile
 }
 
-template <typename T, bool VEC, bool FULL>
+// Sum over the work-group of one value per thread: returns this thread's exclusive prefix (in
+// thread order) and the total through `total`. s_w: kWaves floats of LDS. Every thread calls it.
+__device__ __forceinline__ float block_scan_excl(float x, float* s_w, float& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float incl = x;
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) {
+    const float t = __shfl_up(incl, s);
+    incl = lane >= s ? incl + t : incl;
+  }
+  float excl = __shfl_up(incl, 1);
+  excl = lane == 0 ? 0.0f : excl;
+  if (lane == 63) s_w[wave] = incl;
+  lds_barrier();
+  float before = 0.0f, all = 0.0f;
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v) {
+    before = v < wave ? before + s_w[v] : before;
+    all += s_w[v];
+  }
+  lds_barrier();  // s_w is reused by the caller
+  total = all;
+  return before + excl;
+}
+
+__device__ __forceinline__ float block_max(float x, float* s_w) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) x = fmaxf(x, __shfl_xor(x, s));
+  if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = x;
+  lds_barrier();
+  float r = s_w[0];
+#pragma unroll
+  for (int v = 1; v < kWaves; ++v) r = fmaxf(r, s_w[v]);
+  lds_barrier();
+  return r;
+}
+
+__device__ __forceinline__ int block_min_i(int x, int* s_w) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) x = min(x, __shfl_xor(x, s));
+  if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = x;
+  lds_barrier();
+  int r = s_w[0];
+#pragma unroll
+  for (int v = 1; v < kWaves; ++v) r = min(r, s_w[v]);
+  lds_barrier();
+  return r;
+}
+
+// Work-group b, whose request draws at position k: waits for every work-group's (sm, ss) of the
+// request (its largest stored value and its mass relative to it), scales them to the row's
+// largest value M, and finds the first work-group j (ascending, so ascending vocabulary) whose
+// share of the CDF passes u S, S the row's mass and u the position's uniform clamped to [0, 1]
+// (NaN as 0). Publishes j and the target measured from the start of j's share in j's own scale
+// (j scans its entries for it); past every share (rounding) the last work-group with mass and an
+// infinite target. Without mass the token is 0, after a wait that gave up kResFailed: then the
+// token itself is published, with kNoOwner as the decision.
+__device__ __forceinline__ void res_decide(const ResArgs& a, int b, int k, uint32_t tg, float c,
+                                           bool failed, float* s_f, int* s_i, float* s_tgt1) {
+  const int tid = threadIdx.x;
+  const int j0 = kDecideLoads * tid;
+  const uint64_t* row = a.part + (size_t)b * a.nwg * 2;
+  uint64_t v[2 * kDecideLoads];
+#pragma unroll
+  for (int x = 0; x < 2 * kDecideLoads; ++x) {
+    const int j = j0 + x / 2;
+    v[x] = j < a.nwg ? res_fetch(row + 2 * j + (x & 1)) : (uint64_t)tg << 32;
+  }
+  bool late = false;
+  for (int left = kResSpin;; --left) {
+    bool all = true;
+#pragma unroll
+    for (int x = 0; x < 2 * kDecideLoads; ++x) all = all && (uint32_t)(v[x] >> 32) == tg;
+    if (all) break;
+    if (left == 0) {
+      late = true;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+    for (int x = 0; x < 2 * kDecideLoads; ++x)
+      if ((uint32_t)(v[x] >> 32) != tg) v[x] = res_fetch(row + 2 * (j0 + x / 2) + (x & 1));
+  }
+  float m[kDecideLoads], sraw[kDecideLoads], xs[kDecideLoads];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kDecideLoads; ++i) {
+    const bool live = j0 + i < a.nwg;
+    m[i] = live ? __uint_as_float((uint32_t)v[2 * i]) : -INFINITY;
+    sraw[i] = live ? __uint_as_float((uint32_t)v[2 * i + 1]) : 0.0f;
+    tmax = (sraw[i] > 0.0f && m[i] > tmax) ? m[i] : tmax;
+  }
+  const bool any_late = __syncthreads_or(late) != 0;
+  const float M = block_max(tmax, s_f);
+  float tsum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kDecideLoads; ++i) {
+    xs[i] = sraw[i] > 0.0f
+                ? sraw[i] * (m[i] == M ? 1.0f : __builtin_amdgcn_exp2f((m[i] - M) * c))
+                : 0.0f;
+    tsum += xs[i];
+  }
+  float S;
+  float P = block_scan_excl(tsum, s_f, S);
+  const float u = a.uni[(size_t)b * a.K + k];
+  const float T = (u > 0.0f ? fminf(u, 1.0f) : 0.0f) * S;
+  int found = INT_MAX, last = -1;
+  float tgt = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kDecideLoads; ++i) {
+    if (xs[i] > 0.0f) {
+      if (found == INT_MAX && P + xs[i] > T) {
+        found = j0 + i;
+        tgt = fmaxf(T - P, 0.0f) / xs[i] * sraw[i];  // a fraction of j's share, in j's scale
+      }
+      last = j0 + i;
+    }
+    P += xs[i];
+  }
+  const int jf = block_min_i(found, s_i);
+  if (found == jf && jf != INT_MAX) *s_tgt1 = tgt;
+  const int jl = -block_min_i(-last, s_i);
+  lds_barrier();
+  if (tid == 0) {
+    int token = -1;
+    if (failed || any_late) token = kResFailed;
+    else if (!(S > 0.0f) || jl < 0) token = 0;
+    if (token != -1) {
+      a.tokens[(size_t)b * a.K + k] = token;
+      res_publish(a.tok + b, tg, (uint32_t)token);
+      res_publish(a.dec + 2 * b, tg, kNoOwner);
+    } else {
+      const bool hit = jf != INT_MAX;
+      res_publish(a.dec + 2 * b + 1, tg, __float_as_uint(hit ? *s_tgt1 : INFINITY));
+      res_publish(a.dec + 2 * b, tg, (uint32_t)(hit ? jf : jl));
+    }
+  }
+}
+
+// One wave of the work-group that owns request b's draw at position k: the entries of its tiles
+// (vocabulary t0 * kStreamTile up to the tiles' end), read back from the draft row it wrote, are
+// weighed exactly as the tile epilogue weighed them (offset m, the work-group's largest value);
+// the token is the first entry at which the running sum passes `target` (ascending; lane l holds
+// entries l E .. l E + E - 1), else (rounding) the last entry with mass.
+template <typename T>
+__device__ __forceinline__ void res_owner_draw(const ResArgs& a, const T* __restrict__ out, int b,
+                                               int k, uint32_t tg, int t0, int nit, float m,
+                                               float c, float target) {
+  const int lane = threadIdx.x & 63;
+  const int v0 = t0 * kStreamTile;
+  const int vend = (t0 + nit) * kStreamTile < a.V ? (t0 + nit) * kStreamTile : a.V;
+  const int n = vend - v0;  // >= 1: the work-group reported mass
+  const int E = (n + 63) >> 6;  // <= kResItems
+  const T* row = out + ((size_t)b * a.K + k) * (size_t)a.V + v0;
+  float wv[kResItems];
+  float lsum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kResItems; ++i) {
+    const int idx = lane * E + i;
+    const bool ok = i < E && idx < n;
+    const float y = Logit<T>::get(row[ok ? idx : 0]);
+    wv[i] = ok ? draw_weight(y, m, c) : 0.0f;
+    lsum += wv[i];
+  }
+  float incl = lsum;
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) {
+    const float t = __shfl_up(incl, s);
+    incl = lane >= s ? incl + t : incl;
+  }
+  float cum = __shfl_up(incl, 1);
+  cum = lane == 0 ? 0.0f : cum;
+  int pick = -1, lastw = -1;
+#pragma unroll
+  for (int i = 0; i < kResItems; ++i) {
+    if (wv[i] > 0.0f) {
+      cum += wv[i];
+      pick = (pick < 0 && cum > target) ? i : pick;
+      lastw = i;
+    }
+  }
+  pick = pick < 0 ? lastw : pick;
+  const uint64_t hit = __ballot(lsum > 0.0f && incl > target);
+  const uint64_t mass = __ballot(lsum > 0.0f);
+  int L, e;
+  if (hit != 0) {
+    L = __builtin_ctzll(hit);
+    e = __shfl(pick, L);
+  } else if (mass != 0) {
+    L = 63 - __builtin_clzll(mass);
+    e = __shfl(lastw, L);
+  } else {
+    L = 0;
+    e = 0;
+  }
+  const int token = v0 + L * E + e;
+  if (lane == 0) {
+    a.tokens[(size_t)b * a.K + k] = token;
+    res_publish(a.tok + b, tg, (uint32_t)token);
+  }
+}
+
+template <typename T, bool VEC, bool FULL, bool SAMPLED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void
 markov_resident(const T* __restrict__ base, T* __restrict__ out, ResArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sa[kReqBlock][kARow];
@@ -689,9 +933,22 @@ markov_resident(const T* __restrict__ base, T* __restrict__ out, ResArgs a) {
   __shared__ int s_tok[kReqBlock];
   __shared__ float s_best[kWaves];
   __shared__ int s_bi[kWaves], s_late[kWaves];
+  // sampled form: per request its mode (0 argmax, 1 draw, 2 invalid), inverse temperature, this
+  // work-group's largest stored value, and the draws this work-group owns
+  __shared__ int s_mode[SAMPLED ? kReqBlock : 1], s_own[SAMPLED ? kReqBlock : 1];
+  __shared__ float s_c[SAMPLED ? kReqBlock : 1], s_m[SAMPLED ? kReqBlock : 1];
+  __shared__ float s_tgt[SAMPLED ? kReqBlock : 1], s_tgt1[1];
   const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = w * a.per;
   const int nit = a.ntile - t0 < a.per ? (a.ntile - t0 > 0 ? a.ntile - t0 : 0) : a.per;
+  if constexpr (SAMPLED) {
+    if (tid < kReqBlock) {
+      const float tau = tid < a.B ? a.tau[tid] : 0.0f;
+      const bool draw = (double)tau >= kTauMin && tau < INFINITY;
+      s_mode[tid] = tau == 0.0f ? 0 : (draw ? 1 : 2);
+      s_c[tid] = draw ? (float)(kLog2e / (double)tau) : 1.0f;
+    }
+  }
   v4u32 f[kResItems][kSteps];
 #pragma unroll
   for (int i = 0; i < kResItems; ++i) {
@@ -726,22 +983,35 @@ markov_resident(const T* __restrict__ base, T* __restrict__ out, ResArgs a) {
     // 2. the work-group's tiles, the base logits of the next one in flight
     float run = -INFINITY;
     int run_i = INT_MAX;
+    const float c = SAMPLED ? s_c[tid >> 2] : 1.0f;
+    float sm = -INFINITY, ss = 0.0f;
 #pragma unroll
     for (int i = 0; i < kResItems; ++i) {
       if (i < nit) {  // uniform
         if (i + 1 < nit)
           load_base<T, VEC>(bb[(i + 1) & 1], base, a.B, a.K, a.V, k, t0 + i + 1, 0);
-        res_tile<T, VEC, FULL>(a, out, sa, sz, k, t0 + i, f[i], bb[i & 1], run, run_i);
+        res_tile<T, VEC, FULL, SAMPLED>(a, out, sa, sz, k, t0 + i, f[i], bb[i & 1], run, run_i,
+                                        c, sm, ss);
       }
     }
-    // 3. this work-group's argmax of each request
+    // 3. this work-group's argmax of each request, or (sampled) its largest value and mass
     if ((tid & 3) == 0 && (tid >> 2) < a.B) {
+      const bool draw = SAMPLED && s_mode[tid >> 2] == 1;
       uint64_t* pp = a.part + ((size_t)(tid >> 2) * a.nwg + w) * 2;
-      res_publish(pp, tg, __float_as_uint(run));
-      res_publish(pp + 1, tg, (uint32_t)run_i);
+      res_publish(pp, tg, __float_as_uint(draw ? sm : run));
+      res_publish(pp + 1, tg, draw ? __float_as_uint(ss) : (uint32_t)run_i);
+      if constexpr (SAMPLED) s_m[tid >> 2] = sm;
     }
-    // 4. work-group b < B: the token of request b
-    if (w < a.B) {
+    // 4. work-group b < B: the token of request b (or, drawing, who draws it)
+    const int mode = (SAMPLED && w < a.B) ? s_mode[w] : 0;
+    if (w < a.B && mode == 1) {
+      res_decide(a, w, k, tg, s_c[w], s_tok[w] == kResFailed, s_best, s_bi, s_tgt1);
+    } else if (w < a.B && mode == 2) {
+      if (tid == 0) {
+        a.tokens[(size_t)w * a.K + k] = kInvalid;
+        res_publish(a.tok + w, tg, (uint32_t)kInvalid);
+      }
+    } else if (w < a.B) {
       const int b = w;
       float best = -INFINITY;
       int bi = INT_MAX;
@@ -815,6 +1085,28 @@ markov_resident(const T* __restrict__ base, T* __restrict__ out, ResArgs a) {
         res_publish(a.tok + b, tg, (uint32_t)token);
       }
     }
+    // 5. (sampled) the draws whose CDF target falls in this work-group's tiles
+    if constexpr (SAMPLED) {
+      if (tid < kReqBlock) {
+        int own = 0;
+        float t = 0.0f;
+        if (tid < a.B && s_mode[tid] == 1) {
+          uint32_t pl;
+          if (res_await(a.dec + 2 * tid, tg, pl) && pl == (uint32_t)w) {
+            uint32_t pf;
+            if (res_await(a.dec + 2 * tid + 1, tg, pf)) {
+              own = 1;
+              t = __uint_as_float(pf);
+            }
+          }
+        }
+        s_own[tid] = own;
+        s_tgt[tid] = t;
+      }
+      __syncthreads();  // also: this work-group's stores of the corrected rows are complete
+      for (int b = wave; b < a.B; b += kWaves)
+        if (s_own[b]) res_owner_draw<T>(a, out, b, k, tg, t0, nit, s_m[b], s_c[b], s_tgt[b]);
+    }
     lds_barrier();  // s_tok, s_best are rewritten at the next position
   }
 }
@@ -848,51 +1140,105 @@ uint32_t next_res_tag() {
   return t;
 }
 
+template <typename T, bool SAMPLED>
+const void* resident_kernel(bool full, bool vec_rows) {
+  return full ? (vec_rows ? reinterpret_cast<const void*>(&markov_resident<T, true, true, SAMPLED>)
+                          : reinterpret_cast<const void*>(&markov_resident<T, false, true, SAMPLED>))
+              : (vec_rows ? reinterpret_cast<const void*>(&markov_resident<T, true, false, SAMPLED>)
+                          : reinterpret_cast<const void*>(&markov_resident<T, false, false, SAMPLED>));
+}
+
 // The one-launch form (markov_resident) when it applies: up to 64 requests, ranks up to 256,
 // every tile of the vocabulary in a resident work-group's registers (at most kResItems each),
-// and at least one work-group per request. Returns false when it does not apply.
-template <typename T>
-bool launch_resident(const void* base, void* out, int B, int K, int V, const uint16_t* left,
-                     const uint16_t* right, int R, const int32_t* anchor, int32_t* tokens,
-                     uint64_t* ws, bool vec_rows, hipStream_t s) {
+// and at least one work-group per request (the sampled form: at most kDecideLoads * kThreads
+// work-groups, the partials one decision reads). Sets the kernel, tiles per work-group and
+// work-groups; returns false when it does not apply.
+template <typename T, bool SAMPLED>
+bool resident_plan(int B, int V, int R, bool vec_rows, const void** fn, int* per, int* nwg) {
   if (B > kReqBlock || R > kRankChunk) return false;
   const int ntile = (V + kStreamTile - 1) / kStreamTile;
-  const bool full = R == kRankChunk;
-  const void* fn =
-      full ? (vec_rows ? reinterpret_cast<const void*>(&markov_resident<T, true, true>)
-                       : reinterpret_cast<const void*>(&markov_resident<T, false, true>))
-           : (vec_rows ? reinterpret_cast<const void*>(&markov_resident<T, true, false>)
-                       : reinterpret_cast<const void*>(&markov_resident<T, false, false>));
+  *fn = resident_kernel<T, SAMPLED>(R == kRankChunk, vec_rows);
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, *fn, kThreads, 0) != hipSuccess ||
       per_cu < 1)
     return false;
   const int slots = per_cu * cu_count();
-  const int per = (ntile + slots - 1) / slots;
-  if (per > kResItems) return false;
-  int nwg = (ntile + per - 1) / per;
-  nwg = nwg < B ? B : nwg;
-  if (nwg > slots) return false;
+  *per = (ntile + slots - 1) / slots;
+  if (*per > kResItems) return false;
+  int n = (ntile + *per - 1) / *per;
+  n = n < B ? B : n;
+  if (n > slots || (SAMPLED && n > kDecideLoads * kThreads)) return false;
+  *nwg = n;
+  return true;
+}
+
+// Workspace of one launch of the one-launch form: [B][nwg][2] tagged partials, [B] tagged
+// tokens, [B][2] tagged draw decisions.
+template <typename T, bool SAMPLED>
+void launch_resident_plan(const void* fn, int per, int nwg, const void* base, void* out, int B,
+                          int K, int V, const uint16_t* left, const uint16_t* right, int R,
+                          const int32_t* anchor, const float* tau, const float* uni,
+                          int32_t* tokens, uint64_t* ws, hipStream_t s) {
   ResArgs a;
   a.B = B;
   a.K = K;
   a.V = V;
   a.R = R;
   a.ns = (R + 31) / 32;
-  a.ntile = ntile;
+  a.ntile = (V + kStreamTile - 1) / kStreamTile;
   a.per = per;
   a.nwg = nwg;
   a.left = left;
   a.right = right;
   a.anchor = anchor;
   a.tokens = tokens;
-  a.part = ws;                         // [B][nwg][2]
-  a.tok = ws + (size_t)2 * B * nwg;    // [B]
+  a.part = ws;
+  a.tok = ws + (size_t)2 * B * nwg;
+  a.dec = a.tok + B;
+  a.tau = tau;
+  a.uni = uni;
   a.tag = next_res_tag();
   hipLaunchKernelGGL(
       reinterpret_cast<void (*)(const T*, T*, ResArgs)>(const_cast<void*>(fn)), dim3(nwg),
       dim3(kThreads), 0, s, static_cast<const T*>(base), static_cast<T*>(out), a);
+}
+
+template <typename T>
+bool launch_resident(const void* base, void* out, int B, int K, int V, const uint16_t* left,
+                     const uint16_t* right, int R, const int32_t* anchor, int32_t* tokens,
+                     uint64_t* ws, bool vec_rows, hipStream_t s) {
+  const void* fn = nullptr;
+  int per = 0, nwg = 0;
+  if (!resident_plan<T, false>(B, V, R, vec_rows, &fn, &per, &nwg)) return false;
+  launch_resident_plan<T, false>(fn, per, nwg, base, out, B, K, V, left, right, R, anchor,
+                                 nullptr, nullptr, tokens, ws, s);
   return true;
+}
+
+// The sampled head: the one-launch form in blocks of up to 64 requests, one launch per block,
+// in order on the stream (each block's launch reuses the workspace under its own tag).
+template <typename T>
+int launch_sampled(const void* base, void* out, int B, int K, int V, const uint16_t* left,
+                   const uint16_t* right, int R, const int32_t* anchor, const float* tau,
+                   const float* uni, int32_t* tokens, uint64_t* ws, hipStream_t s) {
+  const bool vec_rows = aligned16(base) && aligned16(out) && ((size_t)V * sizeof(T)) % 16 == 0;
+  for (int b0 = 0; b0 < B; b0 += kReqBlock) {
+    const int nb = B - b0 < kReqBlock ? B - b0 : kReqBlock;
+    const void* fn = nullptr;
+    int per = 0, nwg = 0;
+    if (!resident_plan<T, true>(nb, V, R, vec_rows, &fn, &per, &nwg))
+      return sv_internal_fail(SV_ERR_UNSUPPORTED,
+                              "the sampled head needs R <= 256 and every vocabulary tile in a "
+                              "resident work-group (at most 5 tiles of 64 entries each)");
+    const size_t off = (size_t)b0 * K * V * sizeof(T);
+    launch_resident_plan<T, true>(fn, per, nwg, static_cast<const char*>(base) + off,
+                                  static_cast<char*>(out) + off, nb, K, V, left, right, R,
+                                  anchor != nullptr ? anchor + b0 : nullptr, tau + b0,
+                                  uni + (size_t)b0 * K, tokens + (size_t)b0 * K, ws, s);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return sv_internal_fail(SV_ERR_HIP, hipGetErrorString(e));
+  return SV_OK;
 }
 
 template <typename T>
@@ -951,9 +1297,43 @@ extern "C" size_t sv_markov_workspace_bytes(int B, int V) {
   if (B < 1 || V < 1) return 0;
   const size_t ntile = (V + kStreamTile - 1) / kStreamTile;
   const size_t per_position = (size_t)B * ntile * 8;  // tile partials of the per-position form
-  // one-launch form: [B][nwg][2] tagged partials (nwg <= max(ntile, B)) and [B] tagged tokens
-  const size_t one_launch = (size_t)B * (ntile > (size_t)B ? ntile : (size_t)B) * 16 + (size_t)B * 8;
+  // one launch of the one-launch form (at most 64 requests): [Bl][nwg][2] tagged partials
+  // (nwg <= max(ntile, Bl)), [Bl] tagged tokens, [Bl][2] tagged draw decisions
+  const size_t Bl = B < kReqBlock ? (size_t)B : (size_t)kReqBlock;
+  const size_t one_launch = Bl * (ntile > Bl ? ntile : Bl) * 16 + Bl * 8 + Bl * 16;
   return per_position > one_launch ? per_position : one_launch;
+}
+
+extern "C" int sv_markov_draft_sampled(const void* base_logits, int dtype, int B, int K, int V,
+                                       const uint16_t* left_factor, const uint16_t* right_factor,
+                                       int R, const int32_t* anchor, const float* temperature,
+                                       const float* uniforms, int32_t* draft_tokens,
+                                       void* draft_logits, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  sv_internal_clear_error();
+  if (B < 1 || B > (1 << 20) || K < 1 || K > 64 || V < 1 || V > (1 << 26))
+    return sv_internal_fail(SV_ERR_INVALID_ARG, "need 1 <= B <= 2^20, 1 <= K <= 64, 1 <= V <= 2^26");
+  if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16)
+    return sv_internal_fail(SV_ERR_INVALID_ARG, "dtype must be SV_DTYPE_F32 or SV_DTYPE_BF16");
+  if (R < 16 || R > kMaxRank || R % 16 != 0)
+    return sv_internal_fail(SV_ERR_INVALID_ARG, "rank R must be a multiple of 16 in [16, 1024]");
+  if (!base_logits || !left_factor || !right_factor || !temperature || !uniforms ||
+      !draft_tokens || !draft_logits)
+    return sv_internal_fail(SV_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (reinterpret_cast<uintptr_t>(left_factor) % 16 || reinterpret_cast<uintptr_t>(right_factor) % 16)
+    return sv_internal_fail(SV_ERR_INVALID_ARG, "factors must be 16-byte aligned");
+  const size_t need = sv_markov_workspace_bytes(B, V);
+  if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256)
+    return sv_internal_fail(SV_ERR_WORKSPACE, "workspace missing, too small or not 256-byte aligned");
+  if (R > kRankChunk)
+    return sv_internal_fail(SV_ERR_UNSUPPORTED, "the sampled head needs R <= 256");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint64_t* ws = static_cast<uint64_t*>(workspace);
+  if (dtype == SV_DTYPE_F32)
+    return launch_sampled<float>(base_logits, draft_logits, B, K, V, left_factor, right_factor, R,
+                                 anchor, temperature, uniforms, draft_tokens, ws, s);
+  return launch_sampled<uint16_t>(base_logits, draft_logits, B, K, V, left_factor, right_factor,
+                                  R, anchor, temperature, uniforms, draft_tokens, ws, s);
 }
 
 extern "C" int sv_markov_draft(const void* base_logits, int dtype, int B, int K, int V,

@@ -38,7 +38,9 @@ Readings taken where the pages leave a step open:
     two largest corrected logits are closer than AMBIGUOUS_GAP (a float32 kernel's sum of R
     products may then order them the other way). A draw is ambiguous when its uniform lies closer
     to a CDF boundary than SAMPLE_EPS plus what the kernel's corrected-logit error (at most
-    LOGIT_ABS_TOL + LOGIT_REL_TOL |z|) can move the stored row's CDF (stored_uncertainty).
+    KERNEL_LOGIT_ABS + KERNEL_LOGIT_REL |z|) can move the stored row's CDF (stored_uncertainty).
+    At an ambiguous position every token inside the band is a correct result (valid_tokens);
+    markov_sampled_request can follow a given one of them down the rest of the block.
 """
 from __future__ import annotations
 
@@ -113,9 +115,16 @@ def markov_draft(base: np.ndarray, dtype: str, left: np.ndarray, right: np.ndarr
 # Semi-autoregressive generation; "Bringing DSpark to vLLM Metal", Coming from DFlash); the
 # DSpark article's comparison runs at temperature 1.0 (section 3, evaluation setup).
 
-SAMPLE_EPS = 1e-5     # float32 exp2 and summation error of one draw, relative to the row's mass
-LOGIT_ABS_TOL = 2e-5  # bound on a float32 kernel's corrected logit error: abs + rel * |z|
-LOGIT_REL_TOL = 1e-6
+# A float32 kernel's error in one draw, relative to the row's mass: the weights 2^((y - m) c)
+# carry about 3 roundings of an exponent of at most ~30 (<= 4e-6 of the mass they weigh, at the
+# flattest rows) and the sums of the weights at most ~36 roundings in sequence (<= 2.2e-6); a
+# factor of 2 over the sum.
+SAMPLE_EPS = 1e-5
+# Bound on a float32 kernel's corrected-logit error, abs + rel * |z|: R bf16 products are exact in
+# float32 and only their accumulation rounds (measured at most 1.34e-6 at R = 256 over the
+# Qwen3 vocabulary; the GPU tests hold every float32 output to this bound).
+KERNEL_LOGIT_ABS = 4e-6
+KERNEL_LOGIT_REL = 1e-7
 MARKOV_INVALID = -3   # token of every position of a request whose temperature is invalid
 
 
@@ -148,6 +157,11 @@ def sample_weights(y: np.ndarray, tau: float) -> np.ndarray:
     return np.where(valid, np.exp((np.where(valid, y, m) - m) / tau), 0.0)
 
 
+def clamp_uniform(u: float) -> float:
+    """A draw's uniform as used: NaN and values below 0 read as 0, values above 1 as 1."""
+    return 0.0 if not u > 0.0 else min(float(u), 1.0)
+
+
 def sample_stored_row(y: np.ndarray, tau: float, u: float):
     """One draw from softmax(y / tau) by inverse CDF in ascending vocabulary order with the
     uniform u (NaN and u < 0 read as 0, u >= 1 as 1: the last entry with mass). A row without
@@ -155,16 +169,37 @@ def sample_stored_row(y: np.ndarray, tau: float, u: float):
     w = sample_weights(y, tau)
     if not np.any(w > 0.0):
         return 0, np.inf
-    r = 0.0 if not u > 0.0 else min(float(u), 1.0)
-    return inverse_cdf(w, r)
+    return inverse_cdf(w, clamp_uniform(u))
+
+
+def draw_valid_tokens(y: np.ndarray, tau: float, u: float, band: float) -> np.ndarray:
+    """Tokens with mass whose CDF interval (relative to the row's mass, ascending order) meets
+    [r - band, r + band], r the clamped uniform: every token a draw that errs by at most `band`
+    could return. With band 0 it holds the draw alone (or, on a boundary, both neighbours)."""
+    w = sample_weights(y, tau)
+    if not np.any(w > 0.0):
+        return np.array([0])
+    r = clamp_uniform(u)
+    c = np.cumsum(w) / float(np.sum(w))
+    lo = np.concatenate(([0.0], c[:-1]))
+    hit = (w > 0.0) & (c >= r - band) & (lo <= r + band)
+    if r >= 1.0:
+        hit |= np.arange(len(w)) == np.nonzero(w > 0.0)[0][-1]
+    return np.nonzero(hit)[0]
+
+
+def argmax_valid_tokens(z: np.ndarray) -> np.ndarray:
+    """Entries within AMBIGUOUS_GAP of the largest corrected logit."""
+    z = np.asarray(z, dtype=np.float64)
+    return np.nonzero(z >= z[argmax_lowest(z)] - AMBIGUOUS_GAP)[0]
 
 
 def stored_uncertainty(z: np.ndarray, dtype: str, tau: float) -> float:
     """How far (relative to the row's mass) the CDF of softmax(stored / tau) can move when the
-    kernel's float32 corrected logits lie within LOGIT_ABS_TOL + LOGIT_REL_TOL |z| of the fp64
-    ones: each entry can then be stored as either rounding of the ends of that interval."""
+    kernel's float32 corrected logits lie within KERNEL_LOGIT_ABS + KERNEL_LOGIT_REL |z| of the
+    fp64 ones: each entry can then be stored as either rounding of the ends of that interval."""
     z = np.asarray(z, dtype=np.float64)
-    tol = LOGIT_ABS_TOL + LOGIT_REL_TOL * np.abs(np.where(np.isfinite(z), z, 0.0))
+    tol = KERNEL_LOGIT_ABS + KERNEL_LOGIT_REL * np.abs(np.where(np.isfinite(z), z, 0.0))
     lo = round_stored(z - tol, dtype)
     hi = round_stored(z + tol, dtype)
     mid = round_stored(z, dtype)
@@ -182,7 +217,7 @@ def stored_uncertainty(z: np.ndarray, dtype: str, tau: float) -> float:
 
 
 def markov_sampled_request(base: np.ndarray, dtype: str, left: np.ndarray, right: np.ndarray,
-                           anchor: int, tau: float, uniforms: np.ndarray):
+                           anchor: int, tau: float, uniforms: np.ndarray, choose=None):
     """One request of the sampled head: base [K, V] stored logits; left, right [V, R] bf16 bits;
     tau the request's temperature; uniforms [K] one per position.
 
@@ -194,7 +229,9 @@ def markov_sampled_request(base: np.ndarray, dtype: str, left: np.ndarray, right
 
     Returns (tokens [K], corrected [K, V] fp64, ambiguous [K] bool): position k is ambiguous when
     a float32 kernel may decide it differently (argmax: top-2 gap below AMBIGUOUS_GAP; draw: the
-    CDF margin below SAMPLE_EPS plus stored_uncertainty)."""
+    CDF margin below SAMPLE_EPS plus stored_uncertainty). choose [K] (optional): at an ambiguous
+    position, when choose[k] is one of the tokens valid there (argmax_valid_tokens,
+    draw_valid_tokens), that token is taken instead and biases the next position."""
     K, V = base.shape
     tau = float(tau)
     greedy = tau == 0.0
@@ -213,9 +250,16 @@ def markov_sampled_request(base: np.ndarray, dtype: str, left: np.ndarray, right
         elif greedy:
             y, gap = argmax_with_gap(z)
             amb[k] = gap < AMBIGUOUS_GAP
+            if amb[k] and choose is not None and int(choose[k]) in argmax_valid_tokens(z):
+                y = int(choose[k])
         else:
-            y, margin = sample_stored_row(round_stored(z, dtype), tau, float(uniforms[k]))
-            amb[k] = margin < SAMPLE_EPS + stored_uncertainty(z, dtype, tau)
+            stored = round_stored(z, dtype)
+            y, margin = sample_stored_row(stored, tau, float(uniforms[k]))
+            band = SAMPLE_EPS + stored_uncertainty(z, dtype, tau)
+            amb[k] = margin < band
+            if amb[k] and choose is not None and \
+                    int(choose[k]) in draw_valid_tokens(stored, tau, float(uniforms[k]), band):
+                y = int(choose[k])
         tokens[k] = y
         prev = y
     return tokens, corrected, amb

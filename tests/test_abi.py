@@ -240,3 +240,31 @@ def test_markov_topk_rejects_invalid_arguments(lib, kw, status):
     args.update(kw)
     assert lib.sv_markov_topk(*args.values()) == status
     assert sv.sv_last_error() != ""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), sv.SV_ERR_INVALID_ARG), (dict(K=65), sv.SV_ERR_INVALID_ARG),
+    (dict(V=0), sv.SV_ERR_INVALID_ARG), (dict(dtype=9), sv.SV_ERR_INVALID_ARG),
+    (dict(R=8), sv.SV_ERR_INVALID_ARG), (dict(R=2048), sv.SV_ERR_INVALID_ARG),
+    (dict(base=None), sv.SV_ERR_INVALID_ARG), (dict(tau=None), sv.SV_ERR_INVALID_ARG),
+    (dict(uni=None), sv.SV_ERR_INVALID_ARG), (dict(tokens=None), sv.SV_ERR_INVALID_ARG),
+    (dict(logits=None), sv.SV_ERR_INVALID_ARG), (dict(right=FAKE + 8), sv.SV_ERR_INVALID_ARG),
+    (dict(ws=None), sv.SV_ERR_WORKSPACE), (dict(ws_bytes=8), sv.SV_ERR_WORKSPACE),
+    (dict(ws=WS + 16), sv.SV_ERR_WORKSPACE), (dict(R=512), sv.SV_ERR_UNSUPPORTED),
+])
+def test_markov_sampled_rejects_invalid_arguments(lib, kw, status):
+    args = dict(base=FAKE, dtype=sv.SV_DTYPE_BF16, B=4, K=4, V=1000, left=FAKE, right=FAKE,
+                R=256, anchor=None, tau=FAKE, uni=FAKE, tokens=FAKE, logits=FAKE, ws=WS,
+                ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    assert lib.sv_markov_draft_sampled(*args.values()) == status
+    assert sv.sv_last_error() != ""
+
+
+def test_markov_workspace_holds_the_draw_decisions():
+    lib = sv.load_library()
+    for B, V in [(1, 5), (64, 151936), (64, 100), (200, 151936), (100, 1000)]:
+        ntile = -(-V // 64)
+        Bl = min(B, 64)
+        one_launch = Bl * max(ntile, Bl) * 16 + Bl * 8 + Bl * 16
+        assert lib.sv_markov_workspace_bytes(B, V) >= max(one_launch, B * ntile * 8)

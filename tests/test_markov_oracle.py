@@ -299,12 +299,55 @@ def check_sampled_ambiguity():
     assert t.tolist() == [1] and not amb[0]
 
 
+def check_valid_token_sets():
+    """The valid set of a draw: the draw itself at band 0, both neighbours of a boundary the
+    uniform sits on, every token whose CDF interval meets the band otherwise; the argmax's: the
+    entries within AMBIGUOUS_GAP of the top."""
+    y = np.log(np.array([1.0, 2.0, 3.0, 4.0]))  # CDF 0.1, 0.3, 0.6, 1.0
+    assert M.draw_valid_tokens(y, 1.0, 0.45, 0.0).tolist() == [2]
+    assert M.draw_valid_tokens(y, 1.0, 0.3, 1e-9).tolist() == [1, 2]
+    assert M.draw_valid_tokens(y, 1.0, 0.25, 0.06).tolist() == [1, 2]
+    assert M.draw_valid_tokens(y, 1.0, 0.25, 0.2).tolist() == [0, 1, 2]
+    assert M.draw_valid_tokens(y, 1.0, 0.05, 0.01).tolist() == [0]
+    assert M.draw_valid_tokens(y, 1.0, 7.0, 0.0).tolist() == [3]
+    ninf = np.array([-np.inf, 0.0, -np.inf, 0.0])
+    assert M.draw_valid_tokens(ninf, 1.0, 0.5, 0.1).tolist() == [1, 3]
+    z = np.array([1.0, 3.0, 3.0 - 0.5 * M.AMBIGUOUS_GAP, 3.0 - 2 * M.AMBIGUOUS_GAP])
+    assert M.argmax_valid_tokens(z).tolist() == [1, 2]
+
+
+def check_choose_follows_a_valid_branch():
+    """At a draw that sits on the 'of' / 'no' boundary of the golden example, either token is
+    valid; choosing 'no' makes the next position follow 'no' (its bias), choosing a token
+    outside the valid set changes nothing."""
+    g = json.load(open(os.path.join(HERE, "golden", "markov", "of_course_sampled.json")))
+    base = np.asarray(g["base_logits"], np.float32)
+    L, R = bits(g["left_factor"]), bits(g["right_factor"])
+    w0 = np.exp(np.asarray(g["base_logits"][0], np.float64))
+    edge = float(w0[0] / w0.sum())  # CDF boundary between 'of' and 'no'
+    u = np.array([edge, 0.5])
+    t, _, amb = M.markov_sampled_request(base, "f32", L, R, -1, 1.0, u)
+    assert amb[0] and t[0] in (0, 1)
+    t1, c1, _ = M.markov_sampled_request(base, "f32", L, R, -1, 1.0, u, choose=[1, -9])
+    assert t1.tolist() == [1, 3]
+    assert np.allclose(c1[1], [0.0, 0.0, 0.0, 2.2, 0.3])
+    t0, c0, _ = M.markov_sampled_request(base, "f32", L, R, -1, 1.0, u, choose=[0, -9])
+    assert t0.tolist() == [0, 2] and np.allclose(c0[1], [0.0, 0.0, 2.0, 0.2, 0.3])
+    tx, _, _ = M.markov_sampled_request(base, "f32", L, R, -1, 1.0, u, choose=[4, -9])
+    assert tx.tolist() == t.tolist()
+    # an unambiguous position ignores choose
+    ty, _, amb = M.markov_sampled_request(base, "f32", L, R, -1, 1.0, np.array([0.3, 0.5]),
+                                          choose=[1, 1])
+    assert not amb.any() and ty.tolist() == [0, 2]
+
+
 CHECKS = [check_golden, check_closed_forms, check_bruteforce_bias, check_anchor_rule,
           check_ties_lowest_index, check_topk_golden, check_topk_full_vocabulary_is_the_head,
           check_topk_selection_bruteforce, check_topk_zero_head_and_restriction,
           check_sampled_golden, check_sampled_law, check_sampled_chain_and_tau_zero,
           check_sampled_extremes, check_sampled_invalid_temperature,
-          check_sampled_draws_from_stored_rows, check_sampled_ambiguity]
+          check_sampled_draws_from_stored_rows, check_sampled_ambiguity,
+          check_valid_token_sets, check_choose_follows_a_valid_branch]
 
 
 @pytest.mark.parametrize("chk", CHECKS, ids=lambda f: f.__name__)
@@ -345,23 +388,32 @@ MUTATIONS = {
     "sample_biased_by_argmax": ("        tokens[k] = y\n        prev = y\n    return tokens, corrected, amb",
                                 "        tokens[k] = y\n        prev = argmax_lowest(z) if valid else y\n"
                                 "    return tokens, corrected, amb"),
-    "sample_from_unrounded": ("sample_stored_row(round_stored(z, dtype), tau,",
-                              "sample_stored_row(z, tau,"),
+    "sample_from_unrounded": ("stored = round_stored(z, dtype)", "stored = z"),
     "sample_temperature_dropped": ("np.exp((np.where(valid, y, m) - m) / tau)",
                                    "np.exp(np.where(valid, y, m) - m)"),
-    "sample_descending_cdf": ("    return inverse_cdf(w, r)\n",
-                              "    y, mg = inverse_cdf(w[::-1], r)\n    return len(w) - 1 - y, mg\n"),
+    "sample_descending_cdf": ("    return inverse_cdf(w, clamp_uniform(u))\n",
+                              "    y, mg = inverse_cdf(w[::-1], clamp_uniform(u))\n"
+                              "    return len(w) - 1 - y, mg\n"),
     "sample_nan_has_mass": ("valid = ~np.isnan(y) & (y > -np.inf)\n    if not valid.any():\n"
                             "        return np.zeros_like(y)",
                             "valid = ~(y == -np.inf)\n    if not valid.any():\n"
                             "        return np.zeros_like(y)"),
-    "sample_uniform_unclamped": ("r = 0.0 if not u > 0.0 else min(float(u), 1.0)", "r = float(u)"),
+    "sample_uniform_unclamped": ("return 0.0 if not u > 0.0 else min(float(u), 1.0)",
+                                 "return float(u)"),
     "sample_invalid_tau_accepted": ("valid = greedy or (TAU_MIN <= tau < np.inf)",
                                     "valid = greedy or tau > 0.0"),
     "sample_bf16_truncates": ("np.ldexp(np.rint(np.ldexp(mant, 8)), expo - 8)",
                               "np.ldexp(np.trunc(np.ldexp(mant, 8)), expo - 8)"),
-    "sample_uncertainty_ignored": ("amb[k] = margin < SAMPLE_EPS + stored_uncertainty(z, dtype, tau)",
-                                   "amb[k] = margin < SAMPLE_EPS"),
+    "sample_uncertainty_ignored": ("band = SAMPLE_EPS + stored_uncertainty(z, dtype, tau)",
+                                   "band = SAMPLE_EPS"),
+    "valid_set_misses_lower_neighbour": ("hit = (w > 0.0) & (c >= r - band) & (lo <= r + band)",
+                                         "hit = (w > 0.0) & (c >= r) & (lo <= r + band)"),
+    "valid_set_ignores_band": ("hit = (w > 0.0) & (c >= r - band) & (lo <= r + band)",
+                               "hit = (w > 0.0) & (c > r) & (lo <= r)"),
+    "choose_outside_valid_set": ("int(choose[k]) in draw_valid_tokens(stored, tau, float(uniforms[k]), band)",
+                                 "True"),
+    "argmax_valid_gap_ignored": ("return np.nonzero(z >= z[argmax_lowest(z)] - AMBIGUOUS_GAP)[0]",
+                                 "return np.array([argmax_lowest(z)])"),
 }
 
 

@@ -1,0 +1,189 @@
+"""Sampled Markov-head drafting on the GPU against the oracle's markov_sampled_request.
+
+Parity bar, every position of every request: the token equals the oracle's; at a position the
+oracle marks ambiguous (a draw whose uniform lies closer to a CDF boundary than the kernel's
+float32 arithmetic and logit error can move it, or an argmax whose top-2 gap is below
+AMBIGUOUS_GAP) it is one of the tokens valid there, and the oracle follows it to the next
+position (markov_sampled_request's choose). Draft logits along that chain: float32 within
+KERNEL_LOGIT_ABS + KERNEL_LOGIT_REL |z| of the fp64 value (the bound the oracle's ambiguity band
+assumes), bf16 the float32 value rounded (half a bf16 ulp plus that bound). Temperature 0
+requests are exactly sv_markov_draft's.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+import torch  # noqa: E402
+
+import lossless_draft_verification_sv_amd as sv  # noqa: E402
+import oracle  # noqa: E402
+import workloads  # noqa: E402
+from tests.gpu_util import say, to_dev  # noqa: E402
+
+HERE = os.path.dirname(__file__)
+PEAKED = 14.0  # markov_base lead of a sampling drafter's rows
+
+
+def logit_bound(z, dtype):
+    k = oracle.KERNEL_LOGIT_ABS + oracle.KERNEL_LOGIT_REL * np.abs(z)
+    if dtype == "bf16":
+        return 2.0 ** -8 * np.abs(z) * (1 + 1e-6) + k
+    return k
+
+
+def run(base, left, right, tau, u, anchor):
+    tok, out = sv.sv_markov_draft_sampled(to_dev(base), to_dev(left), to_dev(right),
+                                          to_dev(np.asarray(tau, np.float32)),
+                                          to_dev(np.asarray(u, np.float32)),
+                                          None if anchor is None else to_dev(anchor))
+    torch.cuda.synchronize()
+    logits = (out.float() if out.dtype == torch.bfloat16 else out).cpu().numpy()
+    return tok.cpu().numpy(), logits
+
+
+def check_batch(name, base, dtype, left, right, tau, u, anchor, requests=None):
+    B, K, V = base.shape
+    say(f"[gpu] markov sampled {name}: B={B} K={K} V={V} R={left.shape[1]} {dtype}")
+    tok, logits = run(base, left, right, tau, u, anchor)
+    assert tok.shape == (B, K)
+    idx = range(B) if requests is None else requests
+    exact = valid = 0
+    for b in idx:
+        a = -1 if anchor is None else int(anchor[b])
+        ref_tok, ref_z, amb = oracle.markov_sampled_request(base[b], dtype, left, right, a,
+                                                            float(tau[b]), u[b], choose=tok[b])
+        err = np.abs(logits[b] - ref_z)
+        bad = np.argwhere(err > logit_bound(ref_z, dtype))
+        assert bad.size == 0, (name, b, bad[:5], float(err.max()))
+        assert np.array_equal(tok[b], ref_tok), (name, b, float(tau[b]), u[b], tok[b], ref_tok,
+                                                 amb)
+        valid += int(amb.sum())
+        exact += K - int(amb.sum())
+    say(f"[gpu] markov sampled {name}: {exact} positions exact, {valid} in a valid set")
+    return tok, logits
+
+
+def golden_padded():
+    g = json.load(open(os.path.join(HERE, "golden", "markov", "of_course_sampled.json")))
+    V, R = g["V"], g["R"]
+    left = np.zeros((V, 16), np.float32)
+    right = np.zeros((V, 16), np.float32)
+    left[:, :R] = np.asarray(g["left_factor"], np.float32)
+    right[:, :R] = np.asarray(g["right_factor"], np.float32)
+    return g, workloads.to_bf16_bits(left), workloads.to_bf16_bits(right)
+
+
+def test_golden_of_course_sampled():
+    """Each case of the fixture is one request of a single call."""
+    g, left, right = golden_padded()
+    cases = g["cases"]
+    n = len(cases)
+    base = np.repeat(np.asarray(g["base_logits"], np.float32)[None], n, axis=0)
+    u = np.asarray([c["uniforms"] for c in cases], np.float32)
+    tau = np.full(n, g["temperature"], np.float32)
+    tok, _ = run(base, left, right, tau, u, np.full(n, g["anchor"], np.int32))
+    assert tok.tolist() == [c["tokens"] for c in cases]
+    zero = np.zeros_like(left)
+    tok0, _ = run(base, zero, zero, tau, u, None)
+    assert tok0.tolist() == [c["tokens_without_head"] for c in cases]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,K,V,R", [
+    (70, 5, 1000, 256),  # two launches (64 + 6 requests), a ragged vocabulary tile
+    (1, 3, 5, 16),       # one tile shorter than a wave
+    (64, 2, 4096, 48),   # rank not a multiple of the operand chunk
+    (9, 4, 100003, 128),  # several tiles per work-group, a ragged last tile
+])
+def test_markov_sampled_parity(dtype, B, K, V, R):
+    base = workloads.markov_base(B, K, V, dtype, seed=31 + B + K, lead=PEAKED)
+    left, right = workloads.markov_factors(V, R, seed=32 + V)
+    tau, u = workloads.markov_sampling(B, K, seed=33 + B, greedy_share=0.2,
+                                       temperatures=(1.0, 0.7, 2.0))
+    rng = np.random.default_rng(34 + B)
+    anchor = rng.integers(0, V, size=B).astype(np.int32)
+    anchor[rng.random(B) < 0.2] = -1
+    if B > 2:
+        tau[1] = -1.0          # invalid temperatures: every token -3
+        tau[2] = np.nan
+    check_batch(f"{dtype} B{B} K{K} V{V} R{R}", base, dtype, left, right, tau, u, anchor)
+
+
+def test_markov_sampled_temperature_zero_is_the_argmax_head():
+    B, K, V, R = 12, 4, 3000, 64
+    base = workloads.markov_base(B, K, V, "bf16", seed=35)
+    left, right = workloads.markov_factors(V, R, seed=36)
+    anchor = np.arange(B, dtype=np.int32) * 11
+    u = np.random.default_rng(37).random((B, K)).astype(np.float32)
+    tok, logits = run(base, left, right, np.zeros(B, np.float32), u, anchor)
+    t2, z2 = sv.sv_markov_draft(to_dev(base), to_dev(left), to_dev(right), to_dev(anchor))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(tok, t2.cpu().numpy())
+    np.testing.assert_array_equal(logits, z2.float().cpu().numpy())
+
+
+def test_markov_sampled_extremes():
+    """-inf and NaN entries never drawn; uniforms 0, 1, NaN, negative and above 1; a row
+    without mass; +inf entries."""
+    V = 300
+    zero = np.zeros((V, 16), np.uint16)
+    row = np.full(V, -np.inf, np.float32)
+    row[[7, 100, 299]] = [0.5, 0.25, 1.0]
+    row[[8, 150]] = np.nan
+    u_list = [0.0, 1.0, np.nan, -3.0, 5.0, 0.3, 0.6, 0.99]
+    B = len(u_list) + 2
+    base = np.repeat(row[None, None], B, axis=0)
+    base[len(u_list)] = -np.inf                       # no mass: token 0
+    base[len(u_list) + 1, 0, [3, 200]] = np.inf       # only the +inf entries have mass
+    u = np.asarray(u_list + [0.5, 0.7], np.float32)[:, None]
+    tau = np.ones(B, np.float32)
+    tok, _ = run(base, zero, zero, tau, u, None)
+    want = [oracle.markov_sampled_request(base[b], "f32", zero, zero, -1, 1.0, u[b])[0][0]
+            for b in range(B)]
+    assert tok[:, 0].tolist() == want
+    assert tok[0, 0] == 7 and tok[1, 0] == 299 and tok[2, 0] == 7 and tok[3, 0] == 7
+    assert tok[len(u_list), 0] == 0 and tok[len(u_list) + 1, 0] == 200
+
+
+def test_markov_sampled_law_over_requests():
+    """64 requests share one row; stratified uniforms u_b = (b + 0.5) / 64 walk its CDF: every
+    request matches the oracle and the tokens ascend with b."""
+    B, V = 64, 5000
+    rng = np.random.default_rng(38)
+    row = rng.normal(0, 1.5, V).astype(np.float32)
+    base = np.repeat(row[None, None], B, axis=0)
+    zero = np.zeros((V, 16), np.uint16)
+    u = ((np.arange(B) + 0.5) / B).astype(np.float32)[:, None]
+    tau = np.full(B, 0.5, np.float32)
+    tok, _ = check_batch("law", base, "f32", zero, zero, tau, u, None)
+    assert np.all(np.diff(tok[:, 0]) >= 0)
+
+
+def test_markov_sampled_three_launches_and_repeat():
+    """130 requests: three launches of 64, 64 and 2 requests on one workspace, then the same
+    call again (fresh call tags): identical results."""
+    B, K, V, R = 130, 3, 2500, 32
+    base = workloads.markov_base(B, K, V, "bf16", seed=39, lead=PEAKED)
+    left, right = workloads.markov_factors(V, R, seed=40)
+    tau, u = workloads.markov_sampling(B, K, seed=41, greedy_share=0.3)
+    anchor = np.arange(B, dtype=np.int32)
+    t1, z1 = check_batch("B130", base, "bf16", left, right, tau, u, anchor,
+                         requests=[0, 1, 63, 64, 65, 127, 128, 129])
+    t2, z2 = run(base, left, right, tau, u, anchor)
+    assert np.array_equal(t1, t2) and np.array_equal(z1, z2)
+
+
+def test_markov_sampled_full_size():
+    """The benchmarked shape (64 requests, 8 positions, Qwen3 vocabulary, rank 256, bf16) at
+    temperature 1, eight requests checked against the oracle one by one."""
+    B, K, V, R = 64, 8, workloads.QWEN3_VOCAB, 256
+    base = workloads.markov_base(B, K, V, "bf16", lead=PEAKED)
+    left, right = workloads.markov_factors(V, R)
+    tau, u = workloads.markov_sampling(B, K)
+    anchor = np.random.default_rng(42).integers(0, V, size=B).astype(np.int32)
+    check_batch("full", base, "bf16", left, right, tau, u, anchor,
+                requests=[0, 1, 17, 31, 32, 45, 62, 63])

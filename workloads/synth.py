@@ -322,15 +322,18 @@ def markov_factors(V: int, R: int, seed: int = 1008, sigma: float = 0.25):
     return left, right
 
 
-def markov_base(B: int, K: int, V: int, dtype: str = "bf16", seed: int = 1009) -> np.ndarray:
+def markov_base(B: int, K: int, V: int, dtype: str = "bf16", seed: int = 1009,
+                lead: float = 6.0) -> np.ndarray:
     """Synthetic base logits [B, K, V] of a parallel drafter, stored as `dtype` (bf16 bits or
-    float32): N(0, 2^2) noise plus one favoured token per position at +6, so that a position
-    has a clear leader that the Markov bias (standard deviation about 1 with markov_factors)
-    overturns now and then."""
+    float32): N(0, 2^2) noise plus one favoured token per position at +lead. lead = 6 gives a
+    clear leader that the Markov bias (standard deviation about 1 with markov_factors) overturns
+    now and then; lead = 14 a draft distribution as a sampling drafter meets it, the favoured
+    token holding about half the mass at the Qwen3 vocabulary (most at smaller ones) and the rest
+    spread over the tail."""
     rng = np.random.default_rng(np.random.SeedSequence([seed, B, K, V]))
     z = rng.normal(0.0, 2.0, size=(B, K, V)).astype(np.float32)
-    lead = rng.integers(0, V, size=(B, K))
-    np.put_along_axis(z, lead[..., None], np.take_along_axis(z, lead[..., None], 2) + 6.0, 2)
+    top = rng.integers(0, V, size=(B, K))
+    np.put_along_axis(z, top[..., None], np.take_along_axis(z, top[..., None], 2) + lead, 2)
     return _stored(z, dtype)
 
 
