@@ -34,7 +34,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="batched",
                     help="tiny | interactive | batched | heavy | greedy | mixed | schedule | markov | "
-                         "markov_topk | "
+                         "markov_sampled | markov_topk | "
                          "sweep_<mode>_<K>_<B>_<dtype>")
     ap.add_argument("--min-rotation-bytes", type=float, default=1.2e9,
                     help="rotate input copies until at least this many bytes are cycled")
@@ -280,21 +280,24 @@ def bench_schedule(args):
             f.write(json.dumps(result) + "\n")
 
 
-def bench_markov(args):
+def bench_markov(args, sampled=False):
     """The Markov-head correction (sv_markov_draft) of a draft block: 64 requests, 8 positions,
     the Qwen3 vocabulary, rank-256 synthetic bf16 factors, bf16 base logits. Two copies of the
-    base and output logits alternate between steps."""
+    base and output logits alternate between steps. sampled: the sampled head
+    (sv_markov_draft_sampled) at temperature 1 with one uniform per position, on base logits
+    whose favoured token holds about half the mass (a sampling drafter's rows)."""
     import torch
 
     import lossless_draft_verification_sv_amd as sv
     import oracle
-    from workloads import QWEN3_VOCAB, markov_base, markov_factors
+    from workloads import QWEN3_VOCAB, markov_base, markov_factors, markov_sampling
 
     B, K, V, R = 64, 8, QWEN3_VOCAB, 256
     dev = torch.device("cuda:0")
-    base_h = markov_base(B, K, V, "bf16")
+    base_h = markov_base(B, K, V, "bf16", lead=14.0 if sampled else 6.0)
     left_h, right_h = markov_factors(V, R)
     anchor_h = np.random.default_rng(1010).integers(0, V, size=B).astype(np.int32)
+    tau_h, uni_h = markov_sampling(B, K)
 
     def bf16(a):
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -308,18 +311,28 @@ def bench_markov(args):
     stream = torch.cuda.current_stream(dev)
     ws_bytes = int(lib.sv_markov_workspace_bytes(B, V))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    argv = [[bases[i].data_ptr(), 1, B, K, V, left.data_ptr(), right.data_ptr(), R,
-             anchor.data_ptr(), tokens.data_ptr(), outs[i].data_ptr(), ws.data_ptr(), ws_bytes,
-             stream.cuda_stream] for i in range(2)]
+    if sampled:
+        tau = torch.from_numpy(tau_h).to(dev)
+        uni = torch.from_numpy(uni_h).to(dev)
+        call = lib.sv_markov_draft_sampled
+        argv = [[bases[i].data_ptr(), 1, B, K, V, left.data_ptr(), right.data_ptr(), R,
+                 anchor.data_ptr(), tau.data_ptr(), uni.data_ptr(), tokens.data_ptr(),
+                 outs[i].data_ptr(), ws.data_ptr(), ws_bytes, stream.cuda_stream]
+                for i in range(2)]
+    else:
+        call = lib.sv_markov_draft
+        argv = [[bases[i].data_ptr(), 1, B, K, V, left.data_ptr(), right.data_ptr(), R,
+                 anchor.data_ptr(), tokens.data_ptr(), outs[i].data_ptr(), ws.data_ptr(),
+                 ws_bytes, stream.cuda_stream] for i in range(2)]
     for i in range(max(args.warmup, 2)):
-        if lib.sv_markov_draft(*argv[i % 2]) != 0:
+        if call(*argv[i % 2]) != 0:
             raise RuntimeError(sv.sv_last_error())
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_start = time.perf_counter()
     e0.record(stream)
     for i in range(args.steps):
-        lib.sv_markov_draft(*argv[i % 2])
+        call(*argv[i % 2])
     e1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t_start) * 1e3 / args.steps
@@ -329,6 +342,7 @@ def bench_markov(args):
     # left rows of the previous tokens, K*B*R*2 bytes, and the hand-off words are noise)
     alg = V * R * 2 + K * 2 * B * V * 2
     gbps = alg / (us * 1e-6) / 1e9
+    wl = "markov_sampled_B64_K8_V151936_R256_bf16_t1" if sampled else "markov_B64_K8_V151936_R256_bf16"
     # the oracle on a bounded sample of requests, one by one, its BLAS held to one thread
     from threadpoolctl import threadpool_limits
 
@@ -336,28 +350,35 @@ def bench_markov(args):
     n_req = 0
     with threadpool_limits(limits=1):
         while n_req < B:
-            oracle.markov_draft_request(base_h[n_req], "bf16", left_h, right_h,
-                                        int(anchor_h[n_req]))
+            if sampled:
+                oracle.markov_sampled_request(base_h[n_req], "bf16", left_h, right_h,
+                                              int(anchor_h[n_req]), float(tau_h[n_req]),
+                                              uni_h[n_req])
+            else:
+                oracle.markov_draft_request(base_h[n_req], "bf16", left_h, right_h,
+                                            int(anchor_h[n_req]))
             n_req += 1
             if args.cpu_seconds <= 0 or time.perf_counter() - c0 > args.cpu_seconds:
                 break
     cpu_s = time.perf_counter() - c0
     result = {
-        "metric": "Markov-corrected draft positions/s (sv_markov_draft, B*K positions per call)",
+        "metric": ("sampled Markov draft positions/s (sv_markov_draft_sampled, B*K positions per "
+                   "call)" if sampled else
+                   "Markov-corrected draft positions/s (sv_markov_draft, B*K positions per call)"),
         "value": B * K / (ms_per_step * 1e-3), "unit": "positions/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic N(0, 0.25^2) rank-256 factors and N(0, 2^2) base logits",
-        "config": {"workload": "markov_B64_K8_V151936_R256_bf16", "B": B, "K": K, "V": V,
-                   "R": R},
+        "data": "synthetic N(0, 0.25^2) rank-256 factors and N(0, 2^2) base logits" +
+                (" with a +14 favoured token, temperature 1, seeded uniforms" if sampled else ""),
+        "config": {"workload": wl, "B": B, "K": K, "V": V, "R": R},
         "call_us": {"mean_timed": us},
         "algorithmic_bytes_per_call": alg,
-        "roofline": {"bound": "hbm", "kernel": "sv_markov_draft (markov_resident: one launch, "
-                     "the right factor in registers across positions)", "achieved": gbps,
-                     "peak": HBM_PEAK_GBPS,
+        "roofline": {"bound": "hbm", "kernel": ("sv_markov_draft_sampled" if sampled else
+                                                "sv_markov_draft") +
+                     " (markov_resident: one launch, the right factor in registers across "
+                     "positions)", "achieved": gbps, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic("markov_B64_K8_V151936_R256_bf16",
-                                                 "sv_markov.hip")},
+                     "traffic": measured_traffic(wl, "sv_markov.hip")},
         "cpu_baseline": {"value": n_req * K / cpu_s, "unit": "positions/s", "cores": 1,
                          "kind": "oracle", "sample": f"{n_req} requests x {K} positions, fp64 "
                                                      "numpy, one by one"},
@@ -470,6 +491,8 @@ def main():
         return bench_schedule(args)
     if args.workload == "markov":
         return bench_markov(args)
+    if args.workload == "markov_sampled":
+        return bench_markov(args, sampled=True)
     if args.workload == "markov_topk":
         return bench_markov_topk(args)
     w = pick_workload(args.workload)

@@ -781,50 +781,45 @@ __device__ __forceinline__ int block_min_i(int x, int* s_w) {
 // infinite target. Without mass the token is 0, after a wait that gave up kResFailed: then the
 // token itself is published, with kNoOwner as the decision.
 __device__ __forceinline__ void res_decide(const ResArgs& a, int b, int k, uint32_t tg, float c,
-                                           bool failed, float* s_f, int* s_i, float* s_tgt1) {
+                                           bool failed, float* s_f, int* s_i, float* s_tgt1,
+                                           float* s_pm, float* s_ps) {
   const int tid = threadIdx.x;
-  const int j0 = kDecideLoads * tid;
   const uint64_t* row = a.part + (size_t)b * a.nwg * 2;
-  uint64_t v[2 * kDecideLoads];
-#pragma unroll
-  for (int x = 0; x < 2 * kDecideLoads; ++x) {
-    const int j = j0 + x / 2;
-    v[x] = j < a.nwg ? res_fetch(row + 2 * j + (x & 1)) : (uint64_t)tg << 32;
-  }
+  // the partials into LDS, one per thread at a time
   bool late = false;
-  for (int left = kResSpin;; --left) {
-    bool all = true;
-#pragma unroll
-    for (int x = 0; x < 2 * kDecideLoads; ++x) all = all && (uint32_t)(v[x] >> 32) == tg;
-    if (all) break;
-    if (left == 0) {
-      late = true;
-      break;
+  for (int j0 = 0; j0 < a.nwg; j0 += kThreads) {  // nwg <= kDecideLoads * kThreads
+    const int j = j0 + tid;
+    if (j < a.nwg) {
+      uint64_t v0 = res_fetch(row + 2 * j), v1 = res_fetch(row + 2 * j + 1);
+      for (int left = kResSpin; !late;) {
+        if ((uint32_t)(v0 >> 32) == tg && (uint32_t)(v1 >> 32) == tg) break;
+        if (--left == 0) late = true;
+        __builtin_amdgcn_s_sleep(2);
+        if ((uint32_t)(v0 >> 32) != tg) v0 = res_fetch(row + 2 * j);
+        if ((uint32_t)(v1 >> 32) != tg) v1 = res_fetch(row + 2 * j + 1);
+      }
+      s_pm[j] = __uint_as_float((uint32_t)v0);
+      s_ps[j] = __uint_as_float((uint32_t)v1);
     }
-    __builtin_amdgcn_s_sleep(2);
-#pragma unroll
-    for (int x = 0; x < 2 * kDecideLoads; ++x)
-      if ((uint32_t)(v[x] >> 32) != tg) v[x] = res_fetch(row + 2 * (j0 + x / 2) + (x & 1));
   }
-  float m[kDecideLoads], sraw[kDecideLoads], xs[kDecideLoads];
+  const bool any_late = __syncthreads_or(late) != 0;
+  // thread t: partials kDecideLoads t .. + kDecideLoads - 1 (ascending)
+  const int j0 = kDecideLoads * tid;
   float tmax = -INFINITY;
 #pragma unroll
   for (int i = 0; i < kDecideLoads; ++i) {
-    const bool live = j0 + i < a.nwg;
-    m[i] = live ? __uint_as_float((uint32_t)v[2 * i]) : -INFINITY;
-    sraw[i] = live ? __uint_as_float((uint32_t)v[2 * i + 1]) : 0.0f;
-    tmax = (sraw[i] > 0.0f && m[i] > tmax) ? m[i] : tmax;
+    if (j0 + i < a.nwg && s_ps[j0 + i] > 0.0f) tmax = fmaxf(tmax, s_pm[j0 + i]);
   }
-  const bool any_late = __syncthreads_or(late) != 0;
   const float M = block_max(tmax, s_f);
+  // the share of partial j in the row's scale: s_j 2^((m_j - M) c)
+  auto share = [&](int j) {
+    const float m = s_pm[j], sj = s_ps[j];
+    return sj > 0.0f ? sj * (m == M ? 1.0f : __builtin_amdgcn_exp2f((m - M) * c)) : 0.0f;
+  };
   float tsum = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kDecideLoads; ++i) {
-    xs[i] = sraw[i] > 0.0f
-                ? sraw[i] * (m[i] == M ? 1.0f : __builtin_amdgcn_exp2f((m[i] - M) * c))
-                : 0.0f;
-    tsum += xs[i];
-  }
+  for (int i = 0; i < kDecideLoads; ++i)
+    if (j0 + i < a.nwg) tsum += share(j0 + i);
   float S;
   float P = block_scan_excl(tsum, s_f, S);
   const float u = a.uni[(size_t)b * a.K + k];
@@ -833,14 +828,15 @@ __device__ __forceinline__ void res_decide(const ResArgs& a, int b, int k, uint3
   float tgt = 0.0f;
 #pragma unroll
   for (int i = 0; i < kDecideLoads; ++i) {
-    if (xs[i] > 0.0f) {
-      if (found == INT_MAX && P + xs[i] > T) {
+    const float x = j0 + i < a.nwg ? share(j0 + i) : 0.0f;
+    if (x > 0.0f) {
+      if (found == INT_MAX && P + x > T) {
         found = j0 + i;
-        tgt = fmaxf(T - P, 0.0f) / xs[i] * sraw[i];  // a fraction of j's share, in j's scale
+        tgt = fmaxf(T - P, 0.0f) / x * s_ps[j0 + i];  // a fraction of j's share, in j's scale
       }
       last = j0 + i;
     }
-    P += xs[i];
+    P += x;
   }
   const int jf = block_min_i(found, s_i);
   if (found == jf && jf != INT_MAX) *s_tgt1 = tgt;
@@ -876,17 +872,10 @@ __device__ __forceinline__ void res_owner_draw(const ResArgs& a, const T* __rest
   const int vend = (t0 + nit) * kStreamTile < a.V ? (t0 + nit) * kStreamTile : a.V;
   const int n = vend - v0;  // >= 1: the work-group reported mass
   const int E = (n + 63) >> 6;  // <= kResItems
-  const T* row = out + ((size_t)b * a.K + k) * (size_t)a.V + v0;
-  float wv[kResItems];
+  const T* row = out + ((size_t)b * a.K + k) * (size_t)a.V + v0 + lane * E;
+  const int mine = n - lane * E < E ? n - lane * E : E;  // this lane's entries (may be <= 0)
   float lsum = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kResItems; ++i) {
-    const int idx = lane * E + i;
-    const bool ok = i < E && idx < n;
-    const float y = Logit<T>::get(row[ok ? idx : 0]);
-    wv[i] = ok ? draw_weight(y, m, c) : 0.0f;
-    lsum += wv[i];
-  }
+  for (int i = 0; i < mine; ++i) lsum += draw_weight(Logit<T>::get(row[i]), m, c);
   float incl = lsum;
 #pragma unroll
   for (int s = 1; s < 64; s <<= 1) {
@@ -896,10 +885,10 @@ __device__ __forceinline__ void res_owner_draw(const ResArgs& a, const T* __rest
   float cum = __shfl_up(incl, 1);
   cum = lane == 0 ? 0.0f : cum;
   int pick = -1, lastw = -1;
-#pragma unroll
-  for (int i = 0; i < kResItems; ++i) {
-    if (wv[i] > 0.0f) {
-      cum += wv[i];
+  for (int i = 0; i < mine; ++i) {  // the same weights again (the entries are in the cache)
+    const float w = draw_weight(Logit<T>::get(row[i]), m, c);
+    if (w > 0.0f) {
+      cum += w;
       pick = (pick < 0 && cum > target) ? i : pick;
       lastw = i;
     }
@@ -938,6 +927,8 @@ markov_resident(const T* __restrict__ base, T* __restrict__ out, ResArgs a) {
   __shared__ int s_mode[SAMPLED ? kReqBlock : 1], s_own[SAMPLED ? kReqBlock : 1];
   __shared__ float s_c[SAMPLED ? kReqBlock : 1], s_m[SAMPLED ? kReqBlock : 1];
   __shared__ float s_tgt[SAMPLED ? kReqBlock : 1], s_tgt1[1];
+  __shared__ float s_pm[SAMPLED ? kDecideLoads * kThreads : 1];  // a decision's partials
+  __shared__ float s_ps[SAMPLED ? kDecideLoads * kThreads : 1];
   const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = w * a.per;
   const int nit = a.ntile - t0 < a.per ? (a.ntile - t0 > 0 ? a.ntile - t0 : 0) : a.per;
@@ -1005,7 +996,8 @@ markov_resident(const T* __restrict__ base, T* __restrict__ out, ResArgs a) {
     // 4. work-group b < B: the token of request b (or, drawing, who draws it)
     const int mode = (SAMPLED && w < a.B) ? s_mode[w] : 0;
     if (w < a.B && mode == 1) {
-      res_decide(a, w, k, tg, s_c[w], s_tok[w] == kResFailed, s_best, s_bi, s_tgt1);
+      res_decide(a, w, k, tg, s_c[w], s_tok[w] == kResFailed, s_best, s_bi, s_tgt1, s_pm,
+                 s_ps);
     } else if (w < a.B && mode == 2) {
       if (tid == 0) {
         a.tokens[(size_t)w * a.K + k] = kInvalid;

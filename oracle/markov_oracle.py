@@ -112,7 +112,8 @@ def markov_draft(base: np.ndarray, dtype: str, left: np.ndarray, right: np.ndarr
 # ---------------------------------------------------------------------------------------------
 # Sampled proposals. The pages' head samples each position's token from its corrected
 # distribution and feeds the sample to the next position (DSpark paper review, 4.1
-# Semi-autoregressive generation; "Bringing DSpark to vLLM Metal", Coming from DFlash); the
+# Semi-autoregressive generation; "From draft-then-verify to DSpark", Recovering sequential
+# dependencies); the
 # DSpark article's comparison runs at temperature 1.0 (section 3, evaluation setup).
 
 # A float32 kernel's error in one draw, relative to the row's mass: the weights 2^((y - m) c)
