@@ -187,3 +187,24 @@ def test_markov_sampled_full_size():
     anchor = np.random.default_rng(42).integers(0, V, size=B).astype(np.int32)
     check_batch("full", base, "bf16", left, right, tau, u, anchor,
                 requests=[0, 1, 17, 31, 32, 45, 62, 63])
+
+
+def test_markov_sampled_sixty_four_positions_and_temperature_edges():
+    """K = 64: every draw hand-off of the one-launch form, 64 of them in one call, then the same
+    call again on the same workspace. Temperatures at the edges: the smallest float32 at or
+    above log2(e) / 2^21 (a draw), the float32 just below it and +inf (invalid: -3
+    everywhere)."""
+    B, K, V, R = 6, 64, 600, 32
+    base = workloads.markov_base(B, K, V, "bf16", seed=43, lead=PEAKED)
+    left, right = workloads.markov_factors(V, R, seed=44)
+    lo = np.float32(oracle.TAU_MIN)
+    up = lo if float(lo) >= oracle.TAU_MIN else np.nextafter(lo, np.float32(1.0))
+    below = np.nextafter(up, np.float32(0.0))
+    assert float(up) >= oracle.TAU_MIN > float(below)
+    tau = np.array([1.0, 0.7, 0.0, up, below, np.inf], np.float32)
+    u = np.random.default_rng(45).random((B, K)).astype(np.float32)
+    anchor = np.arange(B, dtype=np.int32) * 7
+    tok1, z1 = check_batch("K64", base, "bf16", left, right, tau, u, anchor)
+    assert np.all(tok1[4] == oracle.MARKOV_INVALID) and np.all(tok1[5] == oracle.MARKOV_INVALID)
+    tok2, z2 = run(base, left, right, tau, u, anchor)
+    assert np.array_equal(tok1, tok2) and np.array_equal(z1, z2)
