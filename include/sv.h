@@ -208,8 +208,9 @@ int sv_schedule_prefix(const float* confidence, int B, int K, const float* step_
  * registers from the first position to the last, and the work-groups hand the positions' tokens
  * to each other through tagged words in the workspace (waits bounded at about 2 s; a token that
  * could not be formed, which needs all of the launch's work-groups not to be resident at once,
- * is reported as -2 at that position and after). Otherwise 2K launches (a bias-and-argmax
- * launch and a finishing launch per position). All on `stream`. Returns SV_OK,
+ * is reported as -2 at that position and after). With 64 < B <= 128 (same conditions
+ * otherwise), one such launch per block of 64 requests, in turn. Otherwise 2K launches (a
+ * bias-and-argmax launch and a finishing launch per position). All on `stream`. Returns SV_OK,
  * SV_ERR_INVALID_ARG, SV_ERR_WORKSPACE, SV_ERR_UNSUPPORTED or SV_ERR_HIP; nothing is launched
  * unless SV_OK.
  */
