@@ -239,14 +239,15 @@ int sv_markov_draft(const void* base_logits, int dtype, int B, int K, int V,
  *  uniforms      [B, K] float, device
  *  draft_logits  [B, K, V] dtype out, device, required (the draws read the stored rows back)
  *  workspace     sv_markov_workspace_bytes(B, V) bytes, as sv_markov_draft
- * The one-launch form of sv_markov_draft only (R <= 256 and every vocabulary tile in a resident
- * work-group), one launch per block of 64 requests, all on `stream`. Within a launch the
+ * Under the one-launch conditions of sv_markov_draft (R <= 256, every vocabulary tile in a
+ * resident work-group), one launch per block of 64 requests, in turn; within a launch the
  * work-groups also hand off each draw: the request's finishing work-group finds which
  * work-group's share of the distribution holds the target, and that work-group finds the token
- * in the entries it wrote. Waits are bounded as in sv_markov_draft (token -2 when one gives up).
- * Returns SV_OK, SV_ERR_INVALID_ARG, SV_ERR_WORKSPACE, SV_ERR_UNSUPPORTED (R > 256, or the
- * vocabulary does not fit the resident work-groups) or SV_ERR_HIP; nothing is launched for
- * SV_ERR_INVALID_ARG, SV_ERR_WORKSPACE or R > 256.
+ * in the entries it wrote (waits bounded as in sv_markov_draft: token -2 when one gives up).
+ * Otherwise 2K launches: sv_markov_draft's per-position tile launch, then a finishing launch
+ * that draws each request's token from its stored row. All on `stream`. Returns SV_OK,
+ * SV_ERR_INVALID_ARG, SV_ERR_WORKSPACE, SV_ERR_UNSUPPORTED or SV_ERR_HIP; nothing is launched
+ * unless SV_OK.
  */
 int sv_markov_draft_sampled(const void* base_logits, int dtype, int B, int K, int V,
                             const uint16_t* left_factor, const uint16_t* right_factor, int R,

@@ -1103,6 +1103,101 @@ markov_resident(const T* __restrict__ base, T* __restrict__ out, ResArgs a) {
   }
 }
 
+// The per-position form's finishing launch for the sampled head: one work-group per request,
+// after position k's tile launch (its draft row is complete in memory). Temperature 0: the
+// argmax over the tile partials, as markov_finish. A drawing temperature: softmax(stored row /
+// tau) by inverse CDF with the position's uniform (clamped to [0, 1], NaN as 0) in ascending
+// vocabulary order; the row's largest stored value is the stored value of the largest tile
+// partial (rounding keeps order); thread t sums the weights of a contiguous chunk of the row, the
+// chunks are scanned in order, and the thread whose chunk holds the target walks it again (the
+// same weights in the same order), else (rounding) the last entry with mass is taken. An invalid
+// temperature: kInvalid.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void markov_finish_sampled(
+    const uint64_t* __restrict__ part, int ntile, int K, int V, int k, const T* __restrict__ out,
+    const float* __restrict__ tau, const float* __restrict__ uni, int32_t* __restrict__ tokens) {
+  __shared__ float s_best[kWaves], s_w[kWaves];
+  __shared__ int s_bi[kWaves], s_i[kWaves];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t* tok = tokens + (size_t)b * K + k;
+  const float t = tau[b];
+  const bool draw = (double)t >= kTauMin && t < INFINITY;
+  if (t != 0.0f && !draw) {  // uniform over the work-group
+    if (tid == 0) *tok = kInvalid;
+    return;
+  }
+  // the argmax over the tile partials (lowest index on ties)
+  const uint64_t* prow = part + (size_t)b * ntile;
+  float best = -INFINITY;
+  int bi = INT_MAX;
+  for (int t0 = 0; t0 < ntile; t0 += kThreads) {
+    if (t0 + tid < ntile) {
+      const uint64_t w = prow[t0 + tid];
+      const float z = __uint_as_float((uint32_t)(w >> 32));
+      const int i = (int)(uint32_t)w;
+      if (better(z, i, best, bi)) {
+        best = z;
+        bi = i;
+      }
+    }
+  }
+  for (int sh = 32; sh >= 1; sh >>= 1) {
+    const float b2 = __shfl_xor(best, sh);
+    const int i2 = __shfl_xor(bi, sh);
+    if (better(b2, i2, best, bi)) {
+      best = b2;
+      bi = i2;
+    }
+  }
+  if (lane == 0) {
+    s_best[wave] = best;
+    s_bi[wave] = bi;
+  }
+  __syncthreads();
+  for (int v = 0; v < kWaves; ++v)
+    if (better(s_best[v], s_bi[v], best, bi)) {
+      best = s_best[v];
+      bi = s_bi[v];
+    }
+  if (!draw || bi == INT_MAX) {  // argmax, or no entry above -inf (token 0); uniform
+    if (tid == 0) *tok = bi == INT_MAX ? 0 : bi;
+    return;
+  }
+  const float m = Logit<T>::stored(best), c = (float)(kLog2e / (double)t);
+  const T* row = out + ((size_t)b * K + k) * (size_t)V;
+  const int chunk = (V + kThreads - 1) / kThreads;
+  const int lo = tid * chunk < V ? tid * chunk : V;
+  const int hi = lo + chunk < V ? lo + chunk : V;
+  float sum = 0.0f;
+  int lastw = -1;
+#pragma unroll 8
+  for (int v = lo; v < hi; ++v) {
+    const float w = draw_weight(Logit<T>::get(row[v]), m, c);
+    sum += w;
+    lastw = w > 0.0f ? v : lastw;
+  }
+  float S;
+  const float P = block_scan_excl(sum, s_w, S);
+  const float u = uni[(size_t)b * K + k];
+  const float target = (u > 0.0f ? fminf(u, 1.0f) : 0.0f) * S;
+  const int owner = block_min_i(sum > 0.0f && P + sum > target ? tid : INT_MAX, s_i);
+  const int last = -block_min_i(-lastw, s_i);
+  if (owner == INT_MAX) {
+    if (tid == 0) *tok = last >= 0 ? last : 0;
+  } else if (tid == owner) {
+    float cum = P;
+    int pick = -1;
+    for (int v = lo; v < hi && pick < 0; ++v) {
+      const float w = draw_weight(Logit<T>::get(row[v]), m, c);
+      if (w > 0.0f) {
+        cum += w;
+        pick = cum > target ? v : pick;
+      }
+    }
+    *tok = pick >= 0 ? pick : lastw;
+  }
+}
+
 bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
 // Compute units of the current device (cached per device).
@@ -1207,43 +1302,20 @@ bool launch_resident(const void* base, void* out, int B, int K, int V, const uin
   return true;
 }
 
-// The sampled head: the one-launch form in blocks of up to 64 requests, one launch per block,
-// in order on the stream (each block's launch reuses the workspace under its own tag).
-template <typename T>
-int launch_sampled(const void* base, void* out, int B, int K, int V, const uint16_t* left,
-                   const uint16_t* right, int R, const int32_t* anchor, const float* tau,
-                   const float* uni, int32_t* tokens, uint64_t* ws, hipStream_t s) {
-  const bool vec_rows = aligned16(base) && aligned16(out) && ((size_t)V * sizeof(T)) % 16 == 0;
-  for (int b0 = 0; b0 < B; b0 += kReqBlock) {
-    const int nb = B - b0 < kReqBlock ? B - b0 : kReqBlock;
-    const void* fn = nullptr;
-    int per = 0, nwg = 0;
-    if (!resident_plan<T, true>(nb, V, R, vec_rows, &fn, &per, &nwg))
-      return sv_internal_fail(SV_ERR_UNSUPPORTED,
-                              "the sampled head needs R <= 256 and every vocabulary tile in a "
-                              "resident work-group (at most 5 tiles of 64 entries each)");
-    const size_t off = (size_t)b0 * K * V * sizeof(T);
-    launch_resident_plan<T, true>(fn, per, nwg, static_cast<const char*>(base) + off,
-                                  static_cast<char*>(out) + off, nb, K, V, left, right, R,
-                                  anchor != nullptr ? anchor + b0 : nullptr, tau + b0,
-                                  uni + (size_t)b0 * K, tokens + (size_t)b0 * K, ws, s);
-  }
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return sv_internal_fail(SV_ERR_HIP, hipGetErrorString(e));
-  return SV_OK;
-}
-
+// tau, uni non-NULL: the sampled head in the per-position form (the finishing launch draws).
 template <typename T>
 int launch_all(const void* base, void* out, int B, int K, int V, const uint16_t* left,
                const uint16_t* right, int R, const int32_t* anchor, int32_t* tokens,
-               uint64_t* part, hipStream_t s) {
+               uint64_t* part, hipStream_t s, const float* tau = nullptr,
+               const float* uni = nullptr) {
   const int nrb = (B + kReqBlock - 1) / kReqBlock;
   const bool stream = R <= kRankChunk;
   const int ntile = stream ? (V + kStreamTile - 1) / kStreamTile : (V + kTileV - 1) / kTileV;
   const int n = ntile * nrb;
   const int groups = 8 * ((n + 7) / 8);
   const bool vec_rows = aligned16(base) && aligned16(out) && ((size_t)V * sizeof(T)) % 16 == 0;
-  if (launch_resident<T>(base, out, B, K, V, left, right, R, anchor, tokens, part, vec_rows, s)) {
+  if (tau == nullptr &&
+      launch_resident<T>(base, out, B, K, V, left, right, R, anchor, tokens, part, vec_rows, s)) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return sv_internal_fail(SV_ERR_HIP, hipGetErrorString(e));
     return SV_OK;
@@ -1253,7 +1325,7 @@ int launch_all(const void* base, void* out, int B, int K, int V, const uint16_t*
   // position; at 256 requests the two are equal)
   const void* fn0 = nullptr;
   int per0 = 0, nwg0 = 0;
-  if (B <= 2 * kReqBlock &&
+  if (tau == nullptr && B <= 2 * kReqBlock &&
       resident_plan<T, false>(kReqBlock, V, R, vec_rows, &fn0, &per0, &nwg0)) {
     for (int b0 = 0; b0 < B; b0 += kReqBlock) {
       const int nb = B - b0 < kReqBlock ? B - b0 : kReqBlock;
@@ -1296,7 +1368,41 @@ int launch_all(const void* base, void* out, int B, int K, int V, const uint16_t*
                          static_cast<const T*>(base), static_cast<T*>(out), B, K, V, k, left,
                          right, R, prev, stride, part, ntile, nrb);
     }
-    hipLaunchKernelGGL(markov_finish, dim3(B), dim3(kThreads), 0, s, part, ntile, K, k, tokens);
+    if (tau != nullptr)
+      hipLaunchKernelGGL(markov_finish_sampled<T>, dim3(B), dim3(kThreads), 0, s, part, ntile, K,
+                         V, k, static_cast<const T*>(out), tau, uni, tokens);
+    else
+      hipLaunchKernelGGL(markov_finish, dim3(B), dim3(kThreads), 0, s, part, ntile, K, k, tokens);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return sv_internal_fail(SV_ERR_HIP, hipGetErrorString(e));
+  return SV_OK;
+}
+
+// The sampled head: the one-launch form in blocks of up to 64 requests, one launch per block,
+// in order on the stream (each block's launch reuses the workspace under its own tag).
+template <typename T>
+int launch_sampled(const void* base, void* out, int B, int K, int V, const uint16_t* left,
+                   const uint16_t* right, int R, const int32_t* anchor, const float* tau,
+                   const float* uni, int32_t* tokens, uint64_t* ws, hipStream_t s) {
+  const bool vec_rows = aligned16(base) && aligned16(out) && ((size_t)V * sizeof(T)) % 16 == 0;
+  {
+    const void* fn = nullptr;
+    int per = 0, nwg = 0;
+    if (!resident_plan<T, true>(B < kReqBlock ? B : kReqBlock, V, R, vec_rows, &fn, &per, &nwg))
+      return launch_all<T>(base, out, B, K, V, left, right, R, anchor, tokens, ws, s, tau, uni);
+  }
+  for (int b0 = 0; b0 < B; b0 += kReqBlock) {
+    const int nb = B - b0 < kReqBlock ? B - b0 : kReqBlock;
+    const void* fn = nullptr;
+    int per = 0, nwg = 0;
+    if (!resident_plan<T, true>(nb, V, R, vec_rows, &fn, &per, &nwg))
+      return sv_internal_fail(SV_ERR_UNSUPPORTED, "a request block did not fit one launch");
+    const size_t off = (size_t)b0 * K * V * sizeof(T);
+    launch_resident_plan<T, true>(fn, per, nwg, static_cast<const char*>(base) + off,
+                                  static_cast<char*>(out) + off, nb, K, V, left, right, R,
+                                  anchor != nullptr ? anchor + b0 : nullptr, tau + b0,
+                                  uni + (size_t)b0 * K, tokens + (size_t)b0 * K, ws, s);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return sv_internal_fail(SV_ERR_HIP, hipGetErrorString(e));
@@ -1337,8 +1443,8 @@ extern "C" int sv_markov_draft_sampled(const void* base_logits, int dtype, int B
   const size_t need = sv_markov_workspace_bytes(B, V);
   if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256)
     return sv_internal_fail(SV_ERR_WORKSPACE, "workspace missing, too small or not 256-byte aligned");
-  if (R > kRankChunk)
-    return sv_internal_fail(SV_ERR_UNSUPPORTED, "the sampled head needs R <= 256");
+  if ((long)((V + kStreamTile - 1) / kStreamTile) * ((B + kReqBlock - 1) / kReqBlock) >= (1L << 30))
+    return sv_internal_fail(SV_ERR_UNSUPPORTED, "grid too large");
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint64_t* ws = static_cast<uint64_t*>(workspace);
   if (dtype == SV_DTYPE_F32)

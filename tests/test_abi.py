@@ -250,7 +250,7 @@ def test_markov_topk_rejects_invalid_arguments(lib, kw, status):
     (dict(uni=None), sv.SV_ERR_INVALID_ARG), (dict(tokens=None), sv.SV_ERR_INVALID_ARG),
     (dict(logits=None), sv.SV_ERR_INVALID_ARG), (dict(right=FAKE + 8), sv.SV_ERR_INVALID_ARG),
     (dict(ws=None), sv.SV_ERR_WORKSPACE), (dict(ws_bytes=8), sv.SV_ERR_WORKSPACE),
-    (dict(ws=WS + 16), sv.SV_ERR_WORKSPACE), (dict(R=512), sv.SV_ERR_UNSUPPORTED),
+    (dict(ws=WS + 16), sv.SV_ERR_WORKSPACE), (dict(R=1040), sv.SV_ERR_INVALID_ARG),
 ])
 def test_markov_sampled_rejects_invalid_arguments(lib, kw, status):
     args = dict(base=FAKE, dtype=sv.SV_DTYPE_BF16, B=4, K=4, V=1000, left=FAKE, right=FAKE,
