@@ -551,6 +551,7 @@ constexpr int32_t kResFailed = -2;
 
 struct ResArgs {
   int B, K, V, R, ns, ntile, per, nwg;
+  int nfull;  // markov_pipe: work-groups w < nfull own per tiles, the others per - 1
   const uint16_t* left;
   const uint16_t* right;
   const int32_t* anchor;
@@ -1103,6 +1104,337 @@ markov_resident(const T* __restrict__ base, T* __restrict__ out, ResArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// The argmax head's one-launch form, pipelined over two halves of the request block. A position
+// runs as two stages, requests 0..31 then 32..63; stage s = 2k + h needs only the tokens of half
+// h at position k - 1, so the hand-off of one half (its partials, the finishing reduction, the
+// token) runs while the work-groups contract the other half's tiles. Work-group b < B finishes
+// request b during the next stage (the other half's), between that stage's second and third
+// tile; one stage past the last position finishes the last half. Everything else is the
+// one-launch form above: the factor words of the work-group's tiles stay in registers, tagged
+// words (the call's tag plus the stage) carry the partials and tokens, every wait is bounded.
+
+// Stages the left-factor rows of half h's previous tokens p (rows 32 h + tid / 32 + 8 u) into sa,
+// then waits for the whole work-group.
+__device__ __forceinline__ void stage_half(uint16_t (*sa)[kARow], const int (&p)[4],
+                                           const uint16_t* __restrict__ left, int R, int r0) {
+  const int sw = threadIdx.x & 31, nw = R / 8;  // 16-byte words per row
+  const int wd = sw < nw ? sw : nw - 1;
+  v4u32 aw[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    aw[u] = reinterpret_cast<const v4u32*>(left + (size_t)(p[u] >= 0 ? p[u] : 0) * R)[wd];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const bool ok = p[u] >= 0 && sw < nw;
+    *reinterpret_cast<v4u32*>(&sa[r0 + (threadIdx.x >> 5) + 8 * u][8 * sw]) =
+        ok ? aw[u] : v4u32{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+}
+
+// Base logits that thread t finishes in a half's tile: row 32 h + t / 8 of the block, columns
+// 8 (t % 8) .. + 7 of the tile (clamped into the batch and the vocabulary; the epilogue masks).
+template <typename T>
+struct HBase {
+  static constexpr int kVec = 16 / (int)sizeof(T);  // logits per 16-byte vector
+  static constexpr int kWords = 8 / kVec;           // vectors of the 8 logits
+  v4u32 w[kWords];
+};
+
+template <typename T>
+__device__ __forceinline__ float hlogit_at(const HBase<T>& bv, int e) {
+  constexpr int kVec = HBase<T>::kVec, kPer32 = 4 / (int)sizeof(T);
+  const uint32_t word = bv.w[e / kVec][(e % kVec) / kPer32];
+  if constexpr (sizeof(T) == 4) return __uint_as_float(word);
+  else return __uint_as_float((e & 1) ? (word & 0xffff0000u) : (word << 16));
+}
+
+template <typename T, bool VEC>
+__device__ __forceinline__ void load_half(HBase<T>& bv, const T* __restrict__ base, int B, int K,
+                                          int V, int k, int tile, int r0) {
+  constexpr int kVec = HBase<T>::kVec;
+  const int tid = threadIdx.x;
+  int b = r0 + (tid >> 3);
+  b = b < B ? b : B - 1;
+  const T* row = base + ((size_t)b * K + k) * (size_t)V;
+#pragma unroll
+  for (int w = 0; w < HBase<T>::kWords; ++w) {
+    const int v0 = tile * kStreamTile + 8 * (tid & 7) + w * kVec;
+    if constexpr (VEC) {
+      bv.w[w] = *reinterpret_cast<const v4u32*>(row + (v0 < V ? v0 : V - kVec));
+    } else {
+      uint32_t e[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        if constexpr (sizeof(T) == 4) {
+          e[x] = __float_as_uint(row[v0 + x < V ? v0 + x : V - 1]);
+        } else {
+          const int v1 = v0 + 2 * x < V ? v0 + 2 * x : V - 1;
+          const int v2 = v0 + 2 * x + 1 < V ? v0 + 2 * x + 1 : V - 1;
+          e[x] = (uint32_t)row[v1] | ((uint32_t)row[v2] << 16);
+        }
+      }
+      bv.w[w] = v4u32{e[0], e[1], e[2], e[3]};
+    }
+  }
+}
+
+// One tile for half h (rows 32 h .. 32 h + 31): every wave contracts its 16 columns for the
+// half's two 16-row blocks; then thread t adds the base logits bv to row 32 h + t / 8, columns
+// 8 (t % 8) .. + 7, writes the corrected logits and folds the argmax into (run, run_i) (every
+// thread of a row holds the row's).
+template <typename T, bool VEC, bool FULL>
+__device__ __forceinline__ void pipe_tile(const ResArgs& a, T* __restrict__ out,
+                                          uint16_t (*sa)[kARow], float (*sz)[kZRow], int k,
+                                          int tile, const v4u32 (&f)[kSteps], const HBase<T>& bv,
+                                          float& run, int& run_i, int h) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r0 = 32 * h;
+  float4_t acc[2] = {{}, {}};
+#pragma unroll
+  for (int t = 0; t < kSteps; ++t) {
+    if (FULL || t < a.ns) {  // uniform
+      const bool inside = FULL || 4 * t + (lane >> 4) < a.R / 8;
+      const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, inside ? f[t] : v4u32{0u, 0u, 0u, 0u});
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const v4u32 x = *reinterpret_cast<const v4u32*>(
+            &sa[r0 + rb * 16 + (lane & 15)][32 * t + 8 * (lane >> 4)]);
+        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x), bfr,
+                                                          acc[rb], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      sz[r0 + rb * 16 + 4 * (lane >> 4) + i][wave * 16 + (lane & 15)] = acc[rb][i];
+  lds_barrier();
+  const int m = r0 + (tid >> 3), q = tid & 7;
+  const int v0 = tile * kStreamTile + 8 * q;
+  if (r0 + 8 * wave < a.B) {  // uniform over the wave
+    float z[8];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const float4 acc4 = *reinterpret_cast<const float4*>(&sz[m][8 * q + 4 * x]);
+      z[4 * x] = hlogit_at<T>(bv, 4 * x) + acc4.x;
+      z[4 * x + 1] = hlogit_at<T>(bv, 4 * x + 1) + acc4.y;
+      z[4 * x + 2] = hlogit_at<T>(bv, 4 * x + 2) + acc4.z;
+      z[4 * x + 3] = hlogit_at<T>(bv, 4 * x + 3) + acc4.w;
+    }
+    const bool row_ok = m < a.B;
+    const int ncol = a.V - v0;
+    float best = -INFINITY;
+    int e_best = -1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bool take = row_ok && e < ncol && z[e] > best;
+      best = take ? z[e] : best;
+      e_best = take ? e : e_best;
+    }
+    int bi = e_best < 0 ? INT_MAX : v0 + e_best;
+    if (out != nullptr && row_ok) {
+      T* orow = out + ((size_t)m * a.K + k) * (size_t)a.V + v0;
+      if constexpr (VEC) {
+        constexpr int kVec = HBase<T>::kVec;
+#pragma unroll
+        for (int w = 0; w < HBase<T>::kWords; ++w) {
+          if (w * kVec < ncol) {
+            if constexpr (sizeof(T) == 4) {
+              *reinterpret_cast<float4*>(orow + 4 * w) =
+                  make_float4(z[4 * w], z[4 * w + 1], z[4 * w + 2], z[4 * w + 3]);
+            } else {
+              uint32_t r[4];
+#pragma unroll
+              for (int x = 0; x < 4; ++x)
+                r[x] = __builtin_bit_cast(uint32_t,
+                                          bf16x2_t{(__bf16)z[2 * x], (__bf16)z[2 * x + 1]});
+              *reinterpret_cast<v4u32*>(orow) = v4u32{r[0], r[1], r[2], r[3]};
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e < ncol) Logit<T>::put(orow + e, z[e]);
+      }
+    }
+#pragma unroll
+    for (int sh = 1; sh <= 4; sh <<= 1) {
+      const float b2 = __shfl_xor(best, sh);
+      const int i2 = __shfl_xor(bi, sh);
+      if (better(b2, i2, best, bi)) {
+        best = b2;
+        bi = i2;
+      }
+    }
+    if (better(best, bi, run, run_i)) {
+      run = best;
+      run_i = bi;
+    }
+  }
+  lds_barrier();  // sz is rewritten by the next tile
+}
+
+template <typename T, bool VEC, bool FULL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void
+markov_pipe(const T* __restrict__ base, T* __restrict__ out, ResArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sa[kReqBlock][kARow];
+  __shared__ __attribute__((aligned(16))) float sz[kReqBlock][kZRow];
+  __shared__ int s_tok[kReqBlock];
+  __shared__ float s_best[kWaves];
+  __shared__ int s_bi[kWaves], s_late[kWaves];
+  const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // work-groups w < nfull own per tiles, the others per - 1 (the last B of them finish requests)
+  const int t0 = w < a.nfull ? w * a.per : a.nfull * a.per + (w - a.nfull) * (a.per - 1);
+  const int nit = w < a.nfull ? a.per : a.per - 1;
+  const int fb = w - (a.nwg - a.B);  // the request this work-group finishes, if fb >= 0
+  v4u32 f[kResItems][kSteps];
+#pragma unroll
+  for (int i = 0; i < kResItems; ++i) {
+    const int tile = t0 + i < a.ntile ? t0 + i : a.ntile - 1;
+    load_factor(f[i], a.right, a.V, a.R, tile);
+  }
+  const int nstage = 2 * a.K;
+  for (int s = 0; s <= nstage; ++s) {
+    const int k = s >> 1, h = s & 1, r0 = 32 * h;
+    // the last stage only finishes; with at most 32 requests the second half has none
+    const bool work = s < nstage && (h == 0 || a.B > 32);
+    const uint32_t tg = a.tag + (uint32_t)s;
+    HBase<T> bb[3];  // the base logits of the next two tiles in flight
+    if (work) {
+      load_half<T, VEC>(bb[0], base, a.B, a.K, a.V, k, t0 < a.ntile ? t0 : a.ntile - 1, r0);
+      if (nit > 1) load_half<T, VEC>(bb[1], base, a.B, a.K, a.V, k, t0 + 1, r0);
+      // 1. the half's previous tokens (the anchors at k = 0)
+      if (tid >= r0 && tid < r0 + 32) {
+        int x = -1;
+        if (tid < a.B) {
+          if (k == 0) {
+            x = a.anchor != nullptr ? a.anchor[tid] : -1;
+          } else {
+            uint32_t pl;
+            x = res_await(a.tok + tid, tg - 2u, pl) ? (int)pl : kResFailed;
+          }
+        }
+        s_tok[tid] = x;
+      }
+      lds_barrier();
+      int p[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int x = s_tok[r0 + (tid >> 5) + 8 * u];
+        p[u] = (x >= 0 && x < a.V) ? x : -1;
+      }
+      stage_half(sa, p, a.left, a.R, r0);
+    }
+    float run = -INFINITY;
+    int run_i = INT_MAX;
+    // 2. the first two tiles
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (work && i < nit) {  // uniform
+        if (i + 2 < nit) load_half<T, VEC>(bb[(i + 2) % 3], base, a.B, a.K, a.V, k, t0 + i + 2, r0);
+        pipe_tile<T, VEC, FULL>(a, out, sa, sz, k, t0 + i, f[i], bb[i % 3], run, run_i, h);
+      }
+    }
+    // 3. the work-group finishing request b, when b is in the other half: the previous stage
+    if (s >= 1 && fb >= 0 && (fb >> 5) == ((s - 1) & 1)) {
+      const int b = fb, kp = (s - 1) >> 1;
+      const uint32_t tp = tg - 1u;
+      float best = -INFINITY;
+      int bi = INT_MAX;
+      bool late = false;
+      for (int j0 = 0; j0 < a.nwg; j0 += 2 * kThreads) {  // two partials per thread in flight
+        const uint64_t* pp[2];
+        uint64_t v[4];
+        bool live[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int j = j0 + u * kThreads + tid;
+          live[u] = j < a.nwg;
+          pp[u] = a.part + ((size_t)b * a.nwg + (live[u] ? j : 0)) * 2;
+          v[2 * u] = live[u] ? res_fetch(pp[u]) : (uint64_t)tp << 32;
+          v[2 * u + 1] = live[u] ? res_fetch(pp[u] + 1) : (uint64_t)tp << 32;
+        }
+        for (int left = kResSpin;; --left) {
+          bool all = true;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) all = all && (uint32_t)(v[x] >> 32) == tp;
+          if (all) break;
+          if (left == 0) {
+            late = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            if ((uint32_t)(v[x] >> 32) != tp) v[x] = res_fetch(pp[x >> 1] + (x & 1));
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          if (live[u]) {
+            const float z = __uint_as_float((uint32_t)v[2 * u]);
+            const int i = (int)(uint32_t)v[2 * u + 1];
+            if (better(z, i, best, bi)) {
+              best = z;
+              bi = i;
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int sh = 32; sh >= 1; sh >>= 1) {
+        const float b2 = __shfl_xor(best, sh);
+        const int i2 = __shfl_xor(bi, sh);
+        if (better(b2, i2, best, bi)) {
+          best = b2;
+          bi = i2;
+        }
+      }
+      const bool wave_late = __ballot(late) != 0;
+      if (lane == 0) {
+        s_best[wave] = best;
+        s_bi[wave] = bi;
+        s_late[wave] = wave_late;
+      }
+      lds_barrier();
+      if (tid == 0) {
+        bool any_late = false;
+        for (int v = 0; v < kWaves; ++v) {
+          any_late = any_late || s_late[v] != 0;
+          if (better(s_best[v], s_bi[v], best, bi)) {
+            best = s_best[v];
+            bi = s_bi[v];
+          }
+        }
+        // s_tok[b] still holds request b's previous token: only its own half's stages write it
+        const bool failed = any_late || s_tok[b] == kResFailed;
+        const int token = failed ? kResFailed : (bi == INT_MAX ? 0 : bi);
+        a.tokens[(size_t)b * a.K + kp] = token;
+        res_publish(a.tok + b, tp, (uint32_t)token);
+      }
+      lds_barrier();  // s_best is rewritten by the next finishing step
+    }
+    // 4. the remaining tiles
+#pragma unroll
+    for (int i = 2; i < kResItems; ++i) {
+      if (work && i < nit) {  // uniform
+        if (i + 2 < nit) load_half<T, VEC>(bb[(i + 2) % 3], base, a.B, a.K, a.V, k, t0 + i + 2, r0);
+        pipe_tile<T, VEC, FULL>(a, out, sa, sz, k, t0 + i, f[i], bb[i % 3], run, run_i, h);
+      }
+    }
+    // 5. this work-group's argmax of each of the half's requests
+    if (work && (tid & 7) == 0 && r0 + (tid >> 3) < a.B) {
+      uint64_t* pp = a.part + ((size_t)(r0 + (tid >> 3)) * a.nwg + w) * 2;
+      res_publish(pp, tg, __float_as_uint(run));
+      res_publish(pp + 1, tg, (uint32_t)run_i);
+    }
+    lds_barrier();  // s_tok is rewritten by the next stage
+  }
+}
+
 // The per-position form's finishing launch for the sampled head: one work-group per request,
 // after position k's tile launch (its draft row is complete in memory). Temperature 0: the
 // argmax over the tile partials, as markov_finish. A drawing temperature: softmax(stored row /
@@ -1215,24 +1547,31 @@ int cu_count() {
   return cached[dev];
 }
 
-// Call tags of the one-launch form: steps of 64, so that tag + k (k < 64) never meets another
-// call's; 0 (a fresh workspace) is never one.
+// Call tags of the one-launch forms: steps of 256, so that tag + k or tag + stage (at most
+// 2 K + 1 = 129 stages) never meets another call's; 0 (a fresh workspace) is never one.
 std::atomic<uint32_t> g_res_tag{0};
 
 uint32_t next_res_tag() {
   uint32_t t;
   do {
-    t = g_res_tag.fetch_add(64u, std::memory_order_relaxed) + 64u;
+    t = g_res_tag.fetch_add(256u, std::memory_order_relaxed) + 256u;
   } while (t == 0);
   return t;
 }
 
+// The argmax head takes the pipelined kernel (markov_pipe), the sampled head markov_resident.
 template <typename T, bool SAMPLED>
 const void* resident_kernel(bool full, bool vec_rows) {
-  return full ? (vec_rows ? reinterpret_cast<const void*>(&markov_resident<T, true, true, SAMPLED>)
-                          : reinterpret_cast<const void*>(&markov_resident<T, false, true, SAMPLED>))
-              : (vec_rows ? reinterpret_cast<const void*>(&markov_resident<T, true, false, SAMPLED>)
-                          : reinterpret_cast<const void*>(&markov_resident<T, false, false, SAMPLED>));
+  if constexpr (!SAMPLED)
+    return full ? (vec_rows ? reinterpret_cast<const void*>(&markov_pipe<T, true, true>)
+                            : reinterpret_cast<const void*>(&markov_pipe<T, false, true>))
+                : (vec_rows ? reinterpret_cast<const void*>(&markov_pipe<T, true, false>)
+                            : reinterpret_cast<const void*>(&markov_pipe<T, false, false>));
+  else
+    return full ? (vec_rows ? reinterpret_cast<const void*>(&markov_resident<T, true, true, true>)
+                            : reinterpret_cast<const void*>(&markov_resident<T, false, true, true>))
+                : (vec_rows ? reinterpret_cast<const void*>(&markov_resident<T, true, false, true>)
+                            : reinterpret_cast<const void*>(&markov_resident<T, false, false, true>));
 }
 
 // The one-launch form (markov_resident) when it applies: up to 64 requests, ranks up to 256,
@@ -1250,6 +1589,14 @@ bool resident_plan(int B, int V, int R, bool vec_rows, const void** fn, int* per
       per_cu < 1)
     return false;
   const int slots = per_cu * cu_count();
+  if constexpr (!SAMPLED) {  // markov_pipe: the tiles over up to ntile + B work-groups, balanced
+    const long want = (long)ntile + B;
+    const int n = want < slots ? (int)want : slots;
+    *per = (ntile + n - 1) / n;
+    if (*per > kResItems || n < B) return false;
+    *nwg = n;
+    return true;
+  }
   *per = (ntile + slots - 1) / slots;
   if (*per > kResItems) return false;
   int n = (ntile + *per - 1) / *per;
@@ -1275,6 +1622,7 @@ void launch_resident_plan(const void* fn, int per, int nwg, const void* base, vo
   a.ntile = (V + kStreamTile - 1) / kStreamTile;
   a.per = per;
   a.nwg = nwg;
+  a.nfull = a.ntile - (per - 1) * nwg;  // markov_pipe's work-groups with per tiles (1 .. nwg)
   a.left = left;
   a.right = right;
   a.anchor = anchor;
@@ -1415,10 +1763,10 @@ extern "C" size_t sv_markov_workspace_bytes(int B, int V) {
   if (B < 1 || V < 1) return 0;
   const size_t ntile = (V + kStreamTile - 1) / kStreamTile;
   const size_t per_position = (size_t)B * ntile * 8;  // tile partials of the per-position form
-  // one launch of the one-launch form (at most 64 requests): [Bl][nwg][2] tagged partials
-  // (nwg <= max(ntile, Bl)), [Bl] tagged tokens, [Bl][2] tagged draw decisions
+  // one launch of the one-launch forms (at most 64 requests): [Bl][nwg][2] tagged partials
+  // (nwg <= ntile + Bl), [Bl] tagged tokens, [Bl][2] tagged draw decisions
   const size_t Bl = B < kReqBlock ? (size_t)B : (size_t)kReqBlock;
-  const size_t one_launch = Bl * (ntile > Bl ? ntile : Bl) * 16 + Bl * 8 + Bl * 16;
+  const size_t one_launch = Bl * (ntile + Bl) * 16 + Bl * 8 + Bl * 16;
   return per_position > one_launch ? per_position : one_launch;
 }
 

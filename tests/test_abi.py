@@ -266,5 +266,5 @@ def test_markov_workspace_holds_the_draw_decisions():
     for B, V in [(1, 5), (64, 151936), (64, 100), (200, 151936), (100, 1000)]:
         ntile = -(-V // 64)
         Bl = min(B, 64)
-        one_launch = Bl * max(ntile, Bl) * 16 + Bl * 8 + Bl * 16
+        one_launch = Bl * (ntile + Bl) * 16 + Bl * 8 + Bl * 16
         assert lib.sv_markov_workspace_bytes(B, V) >= max(one_launch, B * ntile * 8)
