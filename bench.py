@@ -373,10 +373,11 @@ def bench_markov(args, sampled=False):
         "config": {"workload": wl, "B": B, "K": K, "V": V, "R": R},
         "call_us": {"mean_timed": us},
         "algorithmic_bytes_per_call": alg,
-        "roofline": {"bound": "hbm", "kernel": ("sv_markov_draft_sampled" if sampled else
-                                                "sv_markov_draft") +
-                     " (markov_resident: one launch, the right factor in registers across "
-                     "positions)", "achieved": gbps, "peak": HBM_PEAK_GBPS,
+        "roofline": {"bound": "hbm", "kernel": ("sv_markov_draft_sampled (markov_resident"
+                                                if sampled else
+                                                "sv_markov_draft (markov_pipe, two request halves") +
+                     ": one launch, the right factor in registers across positions)",
+                     "achieved": gbps, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(wl, "sv_markov.hip")},
         "cpu_baseline": {"value": n_req * K / cpu_s, "unit": "positions/s", "cores": 1,
