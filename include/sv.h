@@ -205,8 +205,10 @@ int sv_schedule_prefix(const float* confidence, int B, int K, const float* step_
  * With B <= 64 and R <= 256, and when every vocabulary tile fits the registers of a resident
  * work-group (at most five tiles of 64 entries each; V = 151936 on 256 compute units fits), one
  * launch does all K positions: each work-group keeps the right-factor rows of its tiles in
- * registers from the first position to the last, and the work-groups hand the positions' tokens
- * to each other through tagged words in the workspace (waits bounded at about 2 s; a token that
+ * registers from the first position to the last, a position runs as two stages (requests 0..31,
+ * then 32..63) so that one half's token hand-off overlaps the other half's tiles, and the
+ * work-groups hand the tokens to each other through tagged words in the workspace (waits
+ * bounded at about 2 s; a token that
  * could not be formed, which needs all of the launch's work-groups not to be resident at once,
  * is reported as -2 at that position and after). With 64 < B <= 128 (same conditions
  * otherwise), one such launch per block of 64 requests, in turn. Otherwise 2K launches (a
