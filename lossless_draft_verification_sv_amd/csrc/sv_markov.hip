@@ -551,7 +551,7 @@ constexpr int32_t kResFailed = -2;
 
 struct ResArgs {
   int B, K, V, R, ns, ntile, per, nwg;
-  int nfull;  // markov_pipe: work-groups w < nfull own per tiles, the others per - 1
+  int nfull;  // work-groups w < nfull own per tiles, the others per - 1
   const uint16_t* left;
   const uint16_t* right;
   const int32_t* anchor;
@@ -931,8 +931,9 @@ markov_resident(const T* __restrict__ base, T* __restrict__ out, ResArgs a) {
   __shared__ float s_pm[SAMPLED ? kDecideLoads * kThreads : 1];  // a decision's partials
   __shared__ float s_ps[SAMPLED ? kDecideLoads * kThreads : 1];
   const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = w * a.per;
-  const int nit = a.ntile - t0 < a.per ? (a.ntile - t0 > 0 ? a.ntile - t0 : 0) : a.per;
+  // work-groups w < nfull own per tiles, the others per - 1 (contiguous, ascending)
+  const int t0 = w < a.nfull ? w * a.per : a.nfull * a.per + (w - a.nfull) * (a.per - 1);
+  const int nit = w < a.nfull ? a.per : a.per - 1;
   if constexpr (SAMPLED) {
     if (tid < kReqBlock) {
       const float tau = tid < a.B ? a.tau[tid] : 0.0f;
@@ -1588,20 +1589,14 @@ bool resident_plan(int B, int V, int R, bool vec_rows, const void** fn, int* per
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, *fn, kThreads, 0) != hipSuccess ||
       per_cu < 1)
     return false;
-  const int slots = per_cu * cu_count();
-  if constexpr (!SAMPLED) {  // markov_pipe: the tiles over up to ntile + B work-groups, balanced
-    const long want = (long)ntile + B;
-    const int n = want < slots ? (int)want : slots;
-    *per = (ntile + n - 1) / n;
-    if (*per > kResItems || n < B) return false;
-    *nwg = n;
-    return true;
-  }
-  *per = (ntile + slots - 1) / slots;
-  if (*per > kResItems) return false;
-  int n = (ntile + *per - 1) / *per;
-  n = n < B ? B : n;
-  if (n > slots || (SAMPLED && n > kDecideLoads * kThreads)) return false;
+  // the tiles over up to ntile + B work-groups, balanced (the sampled head: at most the
+  // kDecideLoads * kThreads partials a draw decision reads)
+  int cap = per_cu * cu_count();
+  if (SAMPLED && cap > kDecideLoads * kThreads) cap = kDecideLoads * kThreads;
+  const long want = (long)ntile + B;
+  const int n = want < cap ? (int)want : cap;
+  *per = (ntile + n - 1) / n;
+  if (*per > kResItems || n < B) return false;
   *nwg = n;
   return true;
 }
@@ -1622,7 +1617,7 @@ void launch_resident_plan(const void* fn, int per, int nwg, const void* base, vo
   a.ntile = (V + kStreamTile - 1) / kStreamTile;
   a.per = per;
   a.nwg = nwg;
-  a.nfull = a.ntile - (per - 1) * nwg;  // markov_pipe's work-groups with per tiles (1 .. nwg)
+  a.nfull = a.ntile - (per - 1) * nwg;  // work-groups with per tiles (1 .. nwg)
   a.left = left;
   a.right = right;
   a.anchor = anchor;
