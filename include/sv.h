@@ -201,7 +201,10 @@ int sv_schedule_prefix(const float* confidence, int B, int K, const float* step_
  *  workspace     sv_markov_workspace_bytes(B, V) bytes, 256-byte aligned, device, owned by the
  *                caller, no clearing needed between calls of this function. It is left holding
  *                words stamped with this function's own call numbers (or per-tile argmaxes):
- *                zero it before handing the same memory to sv_verify_*.
+ *                zero it before handing the same memory to sv_verify_*. The call numbers are
+ *                a per-process 32-bit count that repeats after 2^24 one-launch calls; memory
+ *                reused by calls of different shapes (B, V, or the sampled head) should be
+ *                zeroed at least that often.
  * With B <= 64 and R <= 256, and when every vocabulary tile fits the registers of a resident
  * work-group (at most five tiles of 64 entries each; V = 151936 on 256 compute units fits), one
  * launch does all K positions: each work-group keeps the right-factor rows of its tiles in
