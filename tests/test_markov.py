@@ -108,6 +108,8 @@ def test_golden_of_course():
     (64, 2, 4096, 48),   # rank not a multiple of the operand chunk
     (3, 4, 300, 1024),   # largest rank
     (130, 1, 257, 32),   # three request blocks, one position, a one-entry last tile
+    (32, 3, 2000, 64),   # one request half: the second half's stages only finish
+    (33, 3, 2000, 64),   # a second half of one request
 ])
 def test_markov_parity(dtype, B, K, V, R):
     base = workloads.markov_base(B, K, V, dtype, seed=11 + B + K)
