@@ -479,7 +479,7 @@ def bench_markov_topk(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (requests are "
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1 (requests are "
                                    "independent: a multi-GPU run would shard the batch)"}))
         sys.exit(2)
 

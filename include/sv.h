@@ -54,7 +54,7 @@ extern "C" {
 typedef enum {
   SV_OK = 0,
   SV_ERR_INVALID_ARG = -1, /* a size, pointer, dtype or temperature is out of range */
-  SV_ERR_UNSUPPORTED = -2, /* a valid request this build does not handle */
+  SV_ERR_UNSUPPORTED = -2, /* a valid request the library does not handle */
   SV_ERR_WORKSPACE = -3,   /* workspace missing, misaligned or smaller than required */
   SV_ERR_HIP = -4          /* the HIP runtime refused a launch */
 } sv_status;
