@@ -100,6 +100,7 @@ def test_golden_of_course_sampled():
     (9, 4, 100003, 128),  # several tiles per work-group, a ragged last tile
     (3, 3, 300, 1024),    # rank above 256: the per-position form (rank passes) and its draw launch
     (2, 2, 200003, 16),   # a vocabulary beyond the resident tiles: the per-position form
+    (70, 2, 700, 512),    # the per-position form over two request blocks
 ])
 def test_markov_sampled_parity(dtype, B, K, V, R):
     base = workloads.markov_base(B, K, V, dtype, seed=31 + B + K, lead=PEAKED)
