@@ -100,23 +100,54 @@ def measured_traffic(workload_name, source="sv_kernels.hip"):
 
 
 def _oracle_request(task):
-    """One request through the fp64 oracle (runs in the bench process or a pool worker)."""
+    """One request through the fp64 oracle (runs in the bench process or a pool worker).
+    Returns (b, k, ambiguous, n, committed, target_prob): the oracle's outputs, which the bench
+    later sets beside the GPU's for the same request."""
     import oracle
 
-    mode, dtype, tau, K, k, target, draft, tokens, uniforms, residual = task
+    b, mode, dtype, tau, K, k, target, draft, tokens, uniforms, residual = task
     if tau > 0:
-        oracle.verify_request(target, draft, dtype, tokens, uniforms, residual, tau, k, K)
-    else:
-        oracle.verify_greedy_request(target, dtype, tokens, k, K)
-    return k
+        r = oracle.verify_request(target, draft, dtype, tokens, uniforms, residual, tau, k, K)
+        return b, k, bool(r.ambiguous), r.n, list(r.committed), list(r.target_prob)
+    n, com = oracle.verify_greedy_request(target, dtype, tokens, k, K)
+    return b, k, False, n, list(com), [0.0] * K
 
 
 def _task(inp, b):
     w = inp.workload
-    return (w.mode, w.dtype, w.temperature_of(b), w.K, inp.k_of(b), inp.target[b],
+    return (b, w.mode, w.dtype, w.temperature_of(b), w.K, inp.k_of(b), inp.target[b],
             None if inp.draft is None else inp.draft[b], inp.tokens[b],
             None if inp.uniforms is None else inp.uniforms[b],
             None if inp.residual is None else float(inp.residual[b]))
+
+
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo ("unknown" where it is not readable)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_check(results, acc, com, tp):
+    """The oracle's outputs for the requests it ran (from the CPU-baseline leg) against the
+    GPU's outputs of the timed calls: requests compared, ambiguous requests (a uniform within
+    1e-6 of a decision threshold: counted, not compared), decision or token mismatches among
+    the others, and the largest |target_prob - oracle|."""
+    amb = mism = 0
+    err = 0.0
+    for b, k, ambiguous, n, committed, target_prob in results.values():
+        if len(tp[b]):
+            err = max(err, float(np.max(np.abs(tp[b] - np.asarray(target_prob)))))
+        if ambiguous:
+            amb += 1
+        elif acc[b] != n or list(com[b]) != list(committed):
+            mism += 1
+    return {"requests": len(results), "ambiguous": amb, "mismatches": mism,
+            "max_target_prob_err": err}
 
 
 def cpu_baseline(inp, budget_s):
@@ -125,15 +156,18 @@ def cpu_baseline(inp, budget_s):
     w = inp.workload
     t0 = time.perf_counter()
     done, positions = 0, 0
+    results = {}
     while done < w.B:
-        positions += _oracle_request(_task(inp, done))
+        r = _oracle_request(_task(inp, done))
+        results[r[0]] = r
+        positions += r[1]
         done += 1
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
     return {"value": positions / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
             "sample": f"first {done} of {w.B} requests of {w.name} ({positions} positions, "
-                      f"{dt:.1f} s, fp64 numpy, one thread)"}
+                      f"{dt:.1f} s, fp64 numpy, one thread)"}, results
 
 
 def cpu_baseline_pool(inp, budget_s, workers):
@@ -145,7 +179,7 @@ def cpu_baseline_pool(inp, budget_s, workers):
     w = inp.workload
     cores = min(workers, len(os.sched_getaffinity(0)))
     if cores < 1:
-        return None
+        return None, {}
     ctx = mp.get_context("spawn")
     saved = os.environ.get("OMP_NUM_THREADS")
     os.environ["OMP_NUM_THREADS"] = "1"  # inherited by the workers: one thread each
@@ -160,6 +194,7 @@ def cpu_baseline_pool(inp, budget_s, workers):
         pool.map(_oracle_request, [_task(inp, 0)] * cores)  # start-up and imports, untimed
         t0 = time.perf_counter()
         done, positions = 0, 0
+        results = {}
         pending = []
         b = 0
         while b < w.B or pending:
@@ -168,12 +203,18 @@ def cpu_baseline_pool(inp, budget_s, workers):
                 b += 1
             if not pending:
                 break
-            positions += pending.pop(0).get()
+            r = pending.pop(0).get()
+            results[r[0]] = r
+            positions += r[1]
             done += 1
         dt = time.perf_counter() - t0
+    avail = len(os.sched_getaffinity(0))
     return {"value": positions / dt, "unit": "positions/s", "cores": cores, "kind": "oracle",
+            "host_cores_available": avail, "cpu_model": cpu_model(),
             "sample": f"{done} of {w.B} requests of {w.name} ({positions} positions, {dt:.1f} s, "
-                      f"fp64 numpy, a pool of {cores} worker processes, one request per task)"}
+                      f"fp64 numpy, a pool of {cores} worker processes, one request per task; "
+                      f"{avail} cores in this process's affinity set, the pool capped at "
+                      f"--cpu-workers {workers}: the GPU box's CPU share for one GPU)"}, results
 
 
 def read_ceiling(lib, call_bytes, dev, stream):
@@ -499,8 +540,8 @@ def main():
     w = pick_workload(args.workload)
     inp = generate(w)
     # the pooled oracle runs first, before this process touches the GPU
-    pooled = (cpu_baseline_pool(inp, args.cpu_seconds, args.cpu_workers)
-              if args.cpu_seconds > 0 and args.cpu_workers > 0 else None)
+    pooled, pooled_results = (cpu_baseline_pool(inp, args.cpu_seconds, args.cpu_workers)
+                              if args.cpu_seconds > 0 and args.cpu_workers > 0 else (None, {}))
     dev = torch.device("cuda:0")
 
     def up(a):
@@ -586,6 +627,9 @@ def main():
 
     alg_bytes, positions = algorithmic_bytes(inp)
     acc_np = acc.cpu().numpy()
+    ks = np.array([inp.k_of(b) for b in range(B)])
+    if not (np.all(acc_np >= 0) and np.all(acc_np <= ks)):
+        raise RuntimeError(f"accepted lengths outside [0, k_b]: {acc_np.tolist()}")
     gbps = alg_bytes / (avg_us * 1e-6) / 1e9
     result = {
         "metric": METRIC,
@@ -598,7 +642,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
+        # the arithmetic type of the path (fp32, with fp64 combines and draws); the logits'
+        # storage type is logit_dtype
         "dtype": "f32",
+        "logit_dtype": w.dtype,
         "data": "synthetic (seeded numpy logits shaped like the pages' workloads; no dataset)",
         "config": {"workload": w.name, "B": B, "K": K, "V": V, "logits": w.dtype,
                    "temperature": w.temperature, "mode": w.mode,
@@ -624,9 +671,13 @@ def main():
         result["read_probe_call_size_gbps"] = same
         result["frac_of_call_size_probe"] = gbps / same
     if args.cpu_seconds > 0:
-        single = cpu_baseline(inp, args.cpu_seconds)
+        single, single_results = cpu_baseline(inp, args.cpu_seconds)
         result["cpu_baseline"] = pooled if pooled is not None else single
         result["cpu_baseline_one_thread"] = single
+        results = pooled_results if len(pooled_results) >= len(single_results) else single_results
+        chk = oracle_check(results, acc_np, com.cpu().numpy(), tp.cpu().numpy())
+        result["oracle_check"] = chk
+        result["ambiguous"] = chk["ambiguous"]
     line = json.dumps(result)
     print(line, flush=True)
     if args.out:

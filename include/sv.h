@@ -32,11 +32,16 @@
  *    read, and may hold anything.
  *  - The workspace: at least sv_workspace_bytes(B, K, V) bytes, 256-byte aligned, owned by the
  *    caller. Within one call, work-groups hand per-chunk partial results to each other through
- *    it, each value stamped with a number drawn fresh for every call, so nothing needs clearing
- *    between calls, of any shape. Zero-fill it once before first use (hipMemset or
- *    torch.zeros): a word of a never-written workspace whose upper half happened to equal a
- *    call's number would be taken for that call's data. One workspace must not be used by two
- *    calls that can run at the same time (e.g. on two streams).
+ *    it, each value stamped with a number drawn fresh for every call (the call counter, shared
+ *    by every entry point of the process), so nothing needs clearing between calls, of any
+ *    shape. The library zero-fills a workspace itself, on `stream` before the launch, on the
+ *    first call that uses it after the call counter's low 32 bits last wrapped and on the first
+ *    call it sees it at all (only the range [workspace, workspace + workspace_bytes) of that
+ *    call, and again for a larger range later): a word left from before a wrap could carry a
+ *    number that is handed out again. Memory that held other data since the library last used
+ *    it as a workspace must be zeroed by the caller (hipMemset or torch.zeros) before it is
+ *    passed again. One workspace must not be used by two calls that can run at the same time
+ *    (e.g. on two streams).
  *  - A work-group waiting for partials from other work-groups of the same call gives up after a
  *    bounded time (about two seconds) and then stores -2 in that request's accepted_len. This
  *    does not happen in normal operation.
@@ -199,25 +204,23 @@ int sv_schedule_prefix(const float* confidence, int B, int K, const float* step_
  *  draft_tokens  [B, K] int32 out; draft_logits [B, K, V] dtype out or NULL (bf16 rounds to
  *                nearest even)
  *  workspace     sv_markov_workspace_bytes(B, V) bytes, 256-byte aligned, device, owned by the
- *                caller, no clearing needed between calls of this function. It is left holding
- *                words stamped with this function's own call numbers (or per-tile argmaxes):
- *                zero it before handing the same memory to sv_verify_*. The call numbers are
- *                a per-process 32-bit count that repeats after 2^24 one-launch calls; memory
- *                reused by calls of different shapes (B, V, or the sampled head) should be
- *                zeroed at least that often.
+ *                caller, no clearing needed between calls of any of the library's functions:
+ *                every one-launch call takes 2K + 2 consecutive numbers of the process's call
+ *                counter and zero-fills the workspace as described for sv_verify_batch, also
+ *                when the per-position form or sv_markov_topk left untagged words in it since.
  * With B <= 64 and R <= 256, and when every vocabulary tile fits the registers of a resident
  * work-group (at most five tiles of 64 entries each; V = 151936 on 256 compute units fits), one
- * launch does all K positions: each work-group keeps the right-factor rows of its tiles in
- * registers from the first position to the last, a position runs as two stages (requests 0..31,
- * then 32..63) so that one half's token hand-off overlaps the other half's tiles, and the
- * work-groups hand the tokens to each other through tagged words in the workspace (waits
- * bounded at about 2 s; a token that
- * could not be formed, which needs all of the launch's work-groups not to be resident at once,
- * is reported as -2 at that position and after). With 64 < B <= 128 (same conditions
- * otherwise), one such launch per block of 64 requests, in turn. Otherwise 2K launches (a
- * bias-and-argmax launch and a finishing launch per position). All on `stream`. Returns SV_OK,
- * SV_ERR_INVALID_ARG, SV_ERR_WORKSPACE, SV_ERR_UNSUPPORTED or SV_ERR_HIP; nothing is launched
- * unless SV_OK.
+ * cooperative launch does all K positions: each work-group keeps the right-factor rows of its
+ * tiles in registers from the first position to the last, a position runs as two stages
+ * (requests 0..31, then 32..63) so that one half's token hand-off overlaps the other half's
+ * tiles, and the work-groups hand the tokens to each other through tagged words in the
+ * workspace. The cooperative launch makes the runtime place every work-group at once or refuse
+ * the launch; a refused launch falls back to the per-position form below. Waits are bounded at
+ * about 2 s all the same (a token that could not be formed is reported as -2 at that position
+ * and after). With 64 < B <= 128 (same conditions otherwise), one such launch per block of 64
+ * requests, in turn. Otherwise 2K launches (a bias-and-argmax launch and a finishing launch per
+ * position). All on `stream`. Returns SV_OK, SV_ERR_INVALID_ARG, SV_ERR_WORKSPACE,
+ * SV_ERR_UNSUPPORTED or SV_ERR_HIP; nothing is launched unless SV_OK.
  */
 size_t sv_markov_workspace_bytes(int B, int V);
 int sv_markov_draft(const void* base_logits, int dtype, int B, int K, int V,
@@ -245,7 +248,8 @@ int sv_markov_draft(const void* base_logits, int dtype, int B, int K, int V,
  *  draft_logits  [B, K, V] dtype out, device, required (the draws read the stored rows back)
  *  workspace     sv_markov_workspace_bytes(B, V) bytes, as sv_markov_draft
  * Under the one-launch conditions of sv_markov_draft (R <= 256, every vocabulary tile in a
- * resident work-group), one launch per block of 64 requests, in turn; within a launch the
+ * resident work-group), one cooperative launch per block of 64 requests, in turn (a refused
+ * launch falls back to the per-position form below); within a launch the
  * work-groups also hand off each draw: the request's finishing work-group finds which
  * work-group's share of the distribution holds the target, and that work-group finds the token
  * in the entries it wrote (waits bounded as in sv_markov_draft: token -2 when one gives up).
@@ -274,7 +278,8 @@ int sv_markov_draft_sampled(const void* base_logits, int dtype, int B, int K, in
  *  draft_tokens  [B, K] int32 out;  candidates [B, K, kc] int32 out or NULL (ascending index)
  *  cand_logits   [B, K, kc] float out or NULL: the corrected logits z of the candidates
  *  workspace     sv_markov_topk_workspace_bytes(B, K, V) bytes, 256-byte aligned, device; no
- *                clearing needed (left holding intermediate tables, not tagged words)
+ *                clearing needed (left holding intermediate tables, not tagged words; a later
+ *                call of another function on the same memory zero-fills it first)
  * Four launches on `stream`. Returns SV_OK, SV_ERR_INVALID_ARG, SV_ERR_UNSUPPORTED (more than
  * 2048 chunk candidates per row: ceil(V / 16384) * kc; 524288 entries at kc = 64),
  * SV_ERR_WORKSPACE or SV_ERR_HIP; nothing is launched unless SV_OK.
@@ -298,6 +303,12 @@ int sv_markov_topk(const void* base_logits, int dtype, int B, int K, int V,
  * Returns SV_OK, SV_ERR_INVALID_ARG (nothing launched) or SV_ERR_HIP.
  */
 int sv_read_probe(const void* data, size_t bytes, uint32_t* partial, int groups, void* stream);
+
+/* Test aid, not a step of the method: sets the process-wide call counter from which every call
+ * draws the numbers that stamp its workspace words (see the workspace convention above), so that
+ * a test can cross a wrap of its low 32 bits without 2^32 calls. Not for use while calls are
+ * being enqueued on another thread. */
+void sv_set_call_counter(uint64_t value);
 
 #ifdef __cplusplus
 }

@@ -79,6 +79,8 @@ def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
         lib.sv_markov_topk.restype = i32
         lib.sv_read_probe.argtypes = [vp, sz, vp, i32, vp]
         lib.sv_read_probe.restype = i32
+        lib.sv_set_call_counter.argtypes = [ctypes.c_uint64]
+        lib.sv_set_call_counter.restype = None
         _lib = lib
         return lib
 
@@ -131,8 +133,11 @@ _ws_cache = {}
 def _workspace(device: torch.device, stream: int, nbytes: int,
                kind: str = "verify") -> torch.Tensor:
     """One cached workspace per (device, stream, kind), zero-filled when allocated: calls on one
-    stream never overlap, and a workspace needs no clearing between calls. The Markov head's
-    workspace is a separate kind: the words it leaves behind carry no call tag."""
+    stream never overlap, and a workspace needs no clearing between calls (the library stamps
+    every word it hands between work-groups with a fresh call number, and zero-fills a workspace
+    itself after its call counter wraps). Kinds that leave untagged words behind get their own
+    workspace: "markov" (the per-position form's tile argmaxes) and "markov_topk" (candidate
+    tables), so that no function reads another's untagged words as tagged ones."""
     key = (device, stream, kind)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
@@ -399,7 +404,7 @@ def sv_markov_topk(base: torch.Tensor, left_factor: torch.Tensor, right_factor: 
     logits = torch.empty(B, K, kc, dtype=torch.float32, device=dev) if return_candidates else None
     stream = torch.cuda.current_stream(dev).cuda_stream
     nbytes = int(lib.sv_markov_topk_workspace_bytes(B, K, V))
-    ws = _workspace(dev, stream, nbytes, "markov")
+    ws = _workspace(dev, stream, nbytes, "markov_topk")
     _check(lib.sv_markov_topk(_ptr(base), _dtype_code(base), B, K, V, _ptr(left_factor),
                               _ptr(right_factor), R, kc, _ptr(anchor), _ptr(tokens), _ptr(cands),
                               _ptr(logits), _ptr(ws), ws.numel(), stream))

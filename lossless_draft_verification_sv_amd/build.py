@@ -11,8 +11,9 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", n) for n in ("sv_kernels.hip", "sv_probe.hip", "sv_schedule.hip",
-                                                "sv_markov.hip", "sv_markov_topk.hip")]
+SRCS = [os.path.join(PKG, "csrc", n) for n in ("sv_kernels.hip", "sv_tags.hip", "sv_probe.hip",
+                                                "sv_schedule.hip", "sv_markov.hip",
+                                                "sv_markov_topk.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsv.so")
 

@@ -42,7 +42,6 @@
 #include <math.h>
 #include <stdint.h>
 
-#include <atomic>
 #include <climits>
 #include <cstdio>
 #include <string>
@@ -1726,18 +1725,6 @@ int launch_status(const char* what) {
   return SV_OK;
 }
 
-// Call tags: every call gets a fresh nonzero number, so words published by earlier calls (or the
-// zeros of a fresh workspace) never pass for this call's.
-std::atomic<uint32_t> g_tag{0};
-
-uint32_t next_tag() {
-  uint32_t t;
-  do {
-    t = g_tag.fetch_add(1, std::memory_order_relaxed) + 1;
-  } while (t == 0);
-  return t;
-}
-
 size_t elem_size(int dtype) { return dtype == SV_DTYPE_F32 ? 4 : 2; }
 
 bool rows_vectorisable(const void* a, const void* b, int dtype, int V) {
@@ -1841,7 +1828,11 @@ int sv_verify_batch(const void* target_logits, const void* draft_logits, int dty
   a.C = p.C;
   a.C2 = p.C2;
   a.NT = p.NT;
-  a.tag = next_tag();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // a fresh call tag: words published by earlier calls (or the zeros of a fresh workspace)
+  // never pass for this call's
+  st = sv_internal_call_tags(1, workspace, workspace_bytes, s, &a.tag);
+  if (st != SV_OK) return st;
   a.stats = reinterpret_cast<uint64_t*>(ws + L.stats);
   a.gath = reinterpret_cast<uint64_t*>(ws + L.gath);
   a.ctot = reinterpret_cast<uint64_t*>(ws + L.ctot);
@@ -1854,7 +1845,6 @@ int sv_verify_batch(const void* target_logits, const void* draft_logits, int dty
   a.t_start = a.d_start = nullptr;
   a.n_trows = a.n_drows = 0;
   a.temps = nullptr;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const bool vec = rows_vectorisable(target_logits, draft_logits, dtype, V);
   a.NS = segments_per_row(V, dtype, vec, p);
   if (dtype == SV_DTYPE_F32)
@@ -1912,7 +1902,9 @@ int sv_verify_ragged(const void* target_logits, const void* draft_logits, int dt
   a.C = p.C;
   a.C2 = p.C2;
   a.NT = p.NT;
-  a.tag = next_tag();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = sv_internal_call_tags(1, workspace, workspace_bytes, s, &a.tag);
+  if (st != SV_OK) return st;
   a.stats = reinterpret_cast<uint64_t*>(ws + L.stats);
   a.gath = reinterpret_cast<uint64_t*>(ws + L.gath);
   a.ctot = reinterpret_cast<uint64_t*>(ws + L.ctot);
@@ -1927,7 +1919,6 @@ int sv_verify_ragged(const void* target_logits, const void* draft_logits, int dt
   a.n_trows = (long)n_target_rows;
   a.n_drows = (long)n_draft_rows;
   a.temps = temperature;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const bool vec = rows_vectorisable(target_logits, a.draft, dtype, V);
   a.NS = segments_per_row(V, dtype, vec, p);
   if (dtype == SV_DTYPE_F32)
@@ -1966,11 +1957,12 @@ int sv_verify_greedy(const void* target_logits, int dtype, int B, int K, int V,
   a.tokens = draft_tokens;
   a.C = p.Cg;
   a.n_argmax_groups = n_argmax;
-  a.tag = next_tag();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = sv_internal_call_tags(1, workspace, workspace_bytes, s, &a.tag);
+  if (st != SV_OK) return st;
   a.gstats = reinterpret_cast<uint64_t*>(ws + L.gstats);
   a.accepted_len = accepted_len;
   a.committed = committed;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const bool vec = rows_vectorisable(target_logits, nullptr, dtype, V);
   if (dtype == SV_DTYPE_F32)
     return vec ? launch_greedy<float, true>(a, groups, s) : launch_greedy<float, false>(a, groups, s);

@@ -17,7 +17,6 @@
 
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 
 #include <float.h>
 #include <limits.h>
@@ -558,7 +557,8 @@ struct ResArgs {
   int32_t* tokens;  // [B][K]
   uint64_t* part;   // [B][nwg][2] tagged (value bits, index) of each work-group's tiles
   uint64_t* tok;    // [B] tagged token of the latest position
-  uint32_t tag;     // position k publishes with tag + k (the host steps tags by 64)
+  uint32_t tag;     // position k (stage s of markov_pipe) publishes with tag + k (tag + s): the
+                    // call owns tags [tag, tag + 2K + 2), at least one past its last stage 2K
   // sampled form only
   const float* tau;  // [B] temperatures: 0 argmax, >= kTauMin and finite a draw, else invalid
   const float* uni;  // [B][K] one uniform per position
@@ -1548,18 +1548,6 @@ int cu_count() {
   return cached[dev];
 }
 
-// Call tags of the one-launch forms: steps of 256, so that tag + k or tag + stage (at most
-// 2 K + 1 = 129 stages) never meets another call's; 0 (a fresh workspace) is never one.
-std::atomic<uint32_t> g_res_tag{0};
-
-uint32_t next_res_tag() {
-  uint32_t t;
-  do {
-    t = g_res_tag.fetch_add(256u, std::memory_order_relaxed) + 256u;
-  } while (t == 0);
-  return t;
-}
-
 // The argmax head takes the pipelined kernel (markov_pipe), the sampled head markov_resident.
 template <typename T, bool SAMPLED>
 const void* resident_kernel(bool full, bool vec_rows) {
@@ -1602,12 +1590,15 @@ bool resident_plan(int B, int V, int R, bool vec_rows, const void** fn, int* per
 }
 
 // Workspace of one launch of the one-launch form: [B][nwg][2] tagged partials, [B] tagged
-// tokens, [B][2] tagged draw decisions.
+// tokens, [B][2] tagged draw decisions. The launch is cooperative: the runtime either makes every
+// work-group of the grid resident at once, which the waits between work-groups rely on, or
+// refuses the launch. Returns SV_OK, SV_ERR_UNSUPPORTED when the cooperative launch was refused
+// (nothing was enqueued but, possibly, the workspace's zero fill), or SV_ERR_HIP.
 template <typename T, bool SAMPLED>
-void launch_resident_plan(const void* fn, int per, int nwg, const void* base, void* out, int B,
-                          int K, int V, const uint16_t* left, const uint16_t* right, int R,
-                          const int32_t* anchor, const float* tau, const float* uni,
-                          int32_t* tokens, uint64_t* ws, hipStream_t s) {
+int launch_resident_plan(const void* fn, int per, int nwg, const void* base, void* out, int B,
+                         int K, int V, const uint16_t* left, const uint16_t* right, int R,
+                         const int32_t* anchor, const float* tau, const float* uni,
+                         int32_t* tokens, uint64_t* ws, size_t ws_bytes, hipStream_t s) {
   ResArgs a;
   a.B = B;
   a.K = K;
@@ -1627,29 +1618,34 @@ void launch_resident_plan(const void* fn, int per, int nwg, const void* base, vo
   a.dec = a.tok + B;
   a.tau = tau;
   a.uni = uni;
-  a.tag = next_res_tag();
-  hipLaunchKernelGGL(
-      reinterpret_cast<void (*)(const T*, T*, ResArgs)>(const_cast<void*>(fn)), dim3(nwg),
-      dim3(kThreads), 0, s, static_cast<const T*>(base), static_cast<T*>(out), a);
+  const int st = sv_internal_call_tags((uint32_t)(2 * K + 2), ws, ws_bytes, s, &a.tag);
+  if (st != SV_OK) return st;
+  const T* base_t = static_cast<const T*>(base);
+  T* out_t = static_cast<T*>(out);
+  void* args[] = {&base_t, &out_t, &a};
+  const hipError_t e = hipLaunchCooperativeKernel(fn, dim3(nwg), dim3(kThreads), args, 0, s);
+  if (e == hipSuccess) return SV_OK;
+  (void)hipGetLastError();  // clear the refusal; the caller takes another form
+  return sv_internal_fail(SV_ERR_UNSUPPORTED, hipGetErrorString(e));
 }
 
+// SV_ERR_UNSUPPORTED when the one-launch form does not apply or its launch was refused.
 template <typename T>
-bool launch_resident(const void* base, void* out, int B, int K, int V, const uint16_t* left,
-                     const uint16_t* right, int R, const int32_t* anchor, int32_t* tokens,
-                     uint64_t* ws, bool vec_rows, hipStream_t s) {
+int launch_resident(const void* base, void* out, int B, int K, int V, const uint16_t* left,
+                    const uint16_t* right, int R, const int32_t* anchor, int32_t* tokens,
+                    uint64_t* ws, size_t ws_bytes, bool vec_rows, hipStream_t s) {
   const void* fn = nullptr;
   int per = 0, nwg = 0;
-  if (!resident_plan<T, false>(B, V, R, vec_rows, &fn, &per, &nwg)) return false;
-  launch_resident_plan<T, false>(fn, per, nwg, base, out, B, K, V, left, right, R, anchor,
-                                 nullptr, nullptr, tokens, ws, s);
-  return true;
+  if (!resident_plan<T, false>(B, V, R, vec_rows, &fn, &per, &nwg)) return SV_ERR_UNSUPPORTED;
+  return launch_resident_plan<T, false>(fn, per, nwg, base, out, B, K, V, left, right, R, anchor,
+                                        nullptr, nullptr, tokens, ws, ws_bytes, s);
 }
 
 // tau, uni non-NULL: the sampled head in the per-position form (the finishing launch draws).
 template <typename T>
 int launch_all(const void* base, void* out, int B, int K, int V, const uint16_t* left,
                const uint16_t* right, int R, const int32_t* anchor, int32_t* tokens,
-               uint64_t* part, hipStream_t s, const float* tau = nullptr,
+               uint64_t* part, size_t ws_bytes, hipStream_t s, const float* tau = nullptr,
                const float* uni = nullptr) {
   const int nrb = (B + kReqBlock - 1) / kReqBlock;
   const bool stream = R <= kRankChunk;
@@ -1657,32 +1653,37 @@ int launch_all(const void* base, void* out, int B, int K, int V, const uint16_t*
   const int n = ntile * nrb;
   const int groups = 8 * ((n + 7) / 8);
   const bool vec_rows = aligned16(base) && aligned16(out) && ((size_t)V * sizeof(T)) % 16 == 0;
-  if (tau == nullptr &&
-      launch_resident<T>(base, out, B, K, V, left, right, R, anchor, tokens, part, vec_rows, s)) {
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return sv_internal_fail(SV_ERR_HIP, hipGetErrorString(e));
-    return SV_OK;
-  }
-  // up to 128 requests: one-launch calls of up to 64 requests in turn (measured faster there
-  // than the per-position form, which reads the factor for every 64-request block at every
-  // position; at 256 requests the two are equal)
-  const void* fn0 = nullptr;
-  int per0 = 0, nwg0 = 0;
-  if (tau == nullptr && B <= 2 * kReqBlock &&
-      resident_plan<T, false>(kReqBlock, V, R, vec_rows, &fn0, &per0, &nwg0)) {
-    for (int b0 = 0; b0 < B; b0 += kReqBlock) {
-      const int nb = B - b0 < kReqBlock ? B - b0 : kReqBlock;
-      const size_t off = (size_t)b0 * K * V * sizeof(T);
-      if (!launch_resident<T>(static_cast<const char*>(base) + off,
-                              out != nullptr ? static_cast<char*>(out) + off : nullptr, nb, K, V,
-                              left, right, R, anchor != nullptr ? anchor + b0 : nullptr,
-                              tokens + (size_t)b0 * K, part, vec_rows, s))
-        return sv_internal_fail(SV_ERR_UNSUPPORTED, "a request block did not fit one launch");
+  if (tau == nullptr && B <= 2 * kReqBlock) {
+    // up to 64 requests: one launch; up to 128: one-launch calls of up to 64 requests in turn
+    // (measured faster there than the per-position form, which reads the factor for every
+    // 64-request block at every position; at 256 requests the two are equal). A refused
+    // cooperative launch falls through to the per-position form below.
+    const void* fn0 = nullptr;
+    int per0 = 0, nwg0 = 0;
+    if (resident_plan<T, false>(B < kReqBlock ? B : kReqBlock, V, R, vec_rows, &fn0, &per0,
+                                &nwg0)) {
+      int st = SV_OK;
+      for (int b0 = 0; b0 < B && st == SV_OK; b0 += kReqBlock) {
+        const int nb = B - b0 < kReqBlock ? B - b0 : kReqBlock;
+        const size_t off = (size_t)b0 * K * V * sizeof(T);
+        st = launch_resident<T>(static_cast<const char*>(base) + off,
+                                out != nullptr ? static_cast<char*>(out) + off : nullptr, nb, K,
+                                V, left, right, R, anchor != nullptr ? anchor + b0 : nullptr,
+                                tokens + (size_t)b0 * K, part, ws_bytes, vec_rows, s);
+      }
+      if (st == SV_OK) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return sv_internal_fail(SV_ERR_HIP, hipGetErrorString(e));
+        return SV_OK;
+      }
+      if (st != SV_ERR_UNSUPPORTED) return st;
+      // a launch was refused: the per-position form below recomputes every request (in stream
+      // order after any block that did run)
+      sv_internal_clear_error();
     }
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return sv_internal_fail(SV_ERR_HIP, hipGetErrorString(e));
-    return SV_OK;
   }
+  // per-position form: its per-tile argmaxes are untagged words
+  sv_internal_untagged_use(part);
   // persistent form: as many work-groups as are resident at once, each a contiguous run of
   // equally many items
   const bool full = R == kRankChunk;
@@ -1727,13 +1728,15 @@ int launch_all(const void* base, void* out, int B, int K, int V, const uint16_t*
 template <typename T>
 int launch_sampled(const void* base, void* out, int B, int K, int V, const uint16_t* left,
                    const uint16_t* right, int R, const int32_t* anchor, const float* tau,
-                   const float* uni, int32_t* tokens, uint64_t* ws, hipStream_t s) {
+                   const float* uni, int32_t* tokens, uint64_t* ws, size_t ws_bytes,
+                   hipStream_t s) {
   const bool vec_rows = aligned16(base) && aligned16(out) && ((size_t)V * sizeof(T)) % 16 == 0;
   {
     const void* fn = nullptr;
     int per = 0, nwg = 0;
     if (!resident_plan<T, true>(B < kReqBlock ? B : kReqBlock, V, R, vec_rows, &fn, &per, &nwg))
-      return launch_all<T>(base, out, B, K, V, left, right, R, anchor, tokens, ws, s, tau, uni);
+      return launch_all<T>(base, out, B, K, V, left, right, R, anchor, tokens, ws, ws_bytes, s,
+                           tau, uni);
   }
   for (int b0 = 0; b0 < B; b0 += kReqBlock) {
     const int nb = B - b0 < kReqBlock ? B - b0 : kReqBlock;
@@ -1742,10 +1745,16 @@ int launch_sampled(const void* base, void* out, int B, int K, int V, const uint1
     if (!resident_plan<T, true>(nb, V, R, vec_rows, &fn, &per, &nwg))
       return sv_internal_fail(SV_ERR_UNSUPPORTED, "a request block did not fit one launch");
     const size_t off = (size_t)b0 * K * V * sizeof(T);
-    launch_resident_plan<T, true>(fn, per, nwg, static_cast<const char*>(base) + off,
-                                  static_cast<char*>(out) + off, nb, K, V, left, right, R,
-                                  anchor != nullptr ? anchor + b0 : nullptr, tau + b0,
-                                  uni + (size_t)b0 * K, tokens + (size_t)b0 * K, ws, s);
+    const int st = launch_resident_plan<T, true>(
+        fn, per, nwg, static_cast<const char*>(base) + off, static_cast<char*>(out) + off, nb, K,
+        V, left, right, R, anchor != nullptr ? anchor + b0 : nullptr, tau + b0,
+        uni + (size_t)b0 * K, tokens + (size_t)b0 * K, ws, ws_bytes, s);
+    if (st == SV_ERR_UNSUPPORTED && b0 == 0) {  // cooperative launch refused: per-position form
+      sv_internal_clear_error();
+      return launch_all<T>(base, out, B, K, V, left, right, R, anchor, tokens, ws, ws_bytes, s,
+                           tau, uni);
+    }
+    if (st != SV_OK) return st;
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return sv_internal_fail(SV_ERR_HIP, hipGetErrorString(e));
@@ -1792,9 +1801,11 @@ extern "C" int sv_markov_draft_sampled(const void* base_logits, int dtype, int B
   uint64_t* ws = static_cast<uint64_t*>(workspace);
   if (dtype == SV_DTYPE_F32)
     return launch_sampled<float>(base_logits, draft_logits, B, K, V, left_factor, right_factor, R,
-                                 anchor, temperature, uniforms, draft_tokens, ws, s);
+                                 anchor, temperature, uniforms, draft_tokens, ws, workspace_bytes,
+                                 s);
   return launch_sampled<uint16_t>(base_logits, draft_logits, B, K, V, left_factor, right_factor,
-                                  R, anchor, temperature, uniforms, draft_tokens, ws, s);
+                                  R, anchor, temperature, uniforms, draft_tokens, ws,
+                                  workspace_bytes, s);
 }
 
 extern "C" int sv_markov_draft(const void* base_logits, int dtype, int B, int K, int V,
@@ -1821,7 +1832,7 @@ extern "C" int sv_markov_draft(const void* base_logits, int dtype, int B, int K,
   uint64_t* part = static_cast<uint64_t*>(workspace);
   if (dtype == SV_DTYPE_F32)
     return launch_all<float>(base_logits, draft_logits, B, K, V, left_factor, right_factor, R,
-                             anchor, draft_tokens, part, s);
+                             anchor, draft_tokens, part, workspace_bytes, s);
   return launch_all<uint16_t>(base_logits, draft_logits, B, K, V, left_factor, right_factor, R,
-                              anchor, draft_tokens, part, s);
+                              anchor, draft_tokens, part, workspace_bytes, s);
 }

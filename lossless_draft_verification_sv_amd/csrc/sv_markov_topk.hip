@@ -702,6 +702,7 @@ extern "C" int sv_markov_topk(const void* base_logits, int dtype, int B, int K, 
     return sv_internal_fail(SV_ERR_WORKSPACE, "workspace missing, too small or not 256-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
+  sv_internal_untagged_use(workspace);  // the tables below are untagged words
   uint64_t* chunks = reinterpret_cast<uint64_t*>(ws + w.chunks);
   int32_t* flag = reinterpret_cast<int32_t*>(ws + w.flag);
   uint32_t* thr = reinterpret_cast<uint32_t*>(ws + w.thr);

@@ -168,12 +168,12 @@ def test_markov_zero_factors_is_per_position_argmax():
 
 def test_markov_full_size_sampled():
     """The benchmarked shape (64 requests, 8 positions, Qwen3 vocabulary, rank 256, bf16) in
-    one call; eight requests checked against the oracle one by one."""
+    one call; every request checked against the oracle one by one."""
     B, K, V, R = 64, 8, workloads.QWEN3_VOCAB, 256
     base = workloads.markov_base(B, K, V, "bf16")
     left, right = workloads.markov_factors(V, R)
     anchor = np.random.default_rng(26).integers(0, V, size=B).astype(np.int32)
-    check_batch("full", base, "bf16", left, right, anchor, requests=[0, 1, 17, 31, 32, 45, 62, 63])
+    check_batch("full", base, "bf16", left, right, anchor)
 
 
 def test_markov_repeat_calls_identical():

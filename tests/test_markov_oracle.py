@@ -3,10 +3,10 @@
 Checked against the pages' worked example (tests/golden/markov/of_course.json), closed forms
 (zero factors leave the base logits; rank-1 factors give a_prev * b_v), a brute-force double
 loop for the bias, and the anchor rule. The top-K variant: the same example with 1, 2 and all
-candidates (tests/golden/markov/of_course_topk.json: one candidate changes the proposal, as the
-pages say candidate limiting can), kc = V equal to the full head, a brute-force sort for the
-selection (ties, NaN, -inf), and a bias that would lift a non-candidate. Planted mistakes must be
-caught.
+candidates (tests/golden/markov/of_course_topk.json: with one candidate the proposal differs
+from the full head's, a restriction the Metal article warns about), kc = V equal to the full
+head, a brute-force sort for the selection (ties, NaN, -inf), and a bias that would lift a
+non-candidate. Planted mistakes must be caught.
 """
 import json
 import os

@@ -174,22 +174,20 @@ def test_markov_sampled_three_launches_and_repeat():
     left, right = workloads.markov_factors(V, R, seed=40)
     tau, u = workloads.markov_sampling(B, K, seed=41, greedy_share=0.3)
     anchor = np.arange(B, dtype=np.int32)
-    t1, z1 = check_batch("B130", base, "bf16", left, right, tau, u, anchor,
-                         requests=[0, 1, 63, 64, 65, 127, 128, 129])
+    t1, z1 = check_batch("B130", base, "bf16", left, right, tau, u, anchor)
     t2, z2 = run(base, left, right, tau, u, anchor)
     assert np.array_equal(t1, t2) and np.array_equal(z1, z2)
 
 
 def test_markov_sampled_full_size():
     """The benchmarked shape (64 requests, 8 positions, Qwen3 vocabulary, rank 256, bf16) at
-    temperature 1, eight requests checked against the oracle one by one."""
+    temperature 1, every request checked against the oracle one by one."""
     B, K, V, R = 64, 8, workloads.QWEN3_VOCAB, 256
     base = workloads.markov_base(B, K, V, "bf16", lead=PEAKED)
     left, right = workloads.markov_factors(V, R)
     tau, u = workloads.markov_sampling(B, K)
     anchor = np.random.default_rng(42).integers(0, V, size=B).astype(np.int32)
-    check_batch("full", base, "bf16", left, right, tau, u, anchor,
-                requests=[0, 1, 17, 31, 32, 45, 62, 63])
+    check_batch("full", base, "bf16", left, right, tau, u, anchor)
 
 
 def test_markov_sampled_sixty_four_positions_and_temperature_edges():

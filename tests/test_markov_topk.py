@@ -121,9 +121,9 @@ def test_topk_ties_nan_and_inf():
 
 def test_topk_full_size_sampled():
     """The benchmarked shape: 64 requests, 8 positions, the Qwen3 vocabulary, rank 256, 64
-    candidates, bf16; eight requests checked one by one."""
+    candidates, bf16; every request checked one by one."""
     B, K, V, R = 64, 8, workloads.QWEN3_VOCAB, 256
     base = workloads.markov_base(B, K, V, "bf16")
     left, right = workloads.markov_factors(V, R)
     anchor = np.random.default_rng(26).integers(0, V, size=B).astype(np.int32)
-    check("full", base, "bf16", left, right, 64, anchor, requests=[0, 5, 17, 31, 32, 46, 62, 63])
+    check("full", base, "bf16", left, right, 64, anchor)
