@@ -107,6 +107,26 @@ int sv_verify_batch(const void* target_logits, const void* draft_logits, int dty
                     float* target_prob, float* draft_prob, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/* sv_verify_batch without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). The
+ * arguments and outputs are those of sv_verify_batch, run by the same kernels; the scratch memory
+ * is a 16 MiB array the library holds on each GPU it runs on (from the first call on that GPU until
+ * the process ends), whose device address it looks up once per device. Nothing is allocated: no
+ * hipMalloc, hipFree or allocating library routine is called. The call runs on the current device
+ * (`stream` must belong to it). Every call on one GPU shares that GPU's array, which keeps the last
+ * call's words: calls that can overlap on one GPU (two streams, two host threads) race and give
+ * undefined results; serialise them. The array is zero-filled on the stream before its first use on
+ * each device (and after a wrap of the call counter), as a workspace is.
+ * Returns what sv_verify_batch returns, or SV_ERR_UNSUPPORTED (nothing launched) when the batch
+ * needs more than 16 MiB of scratch (sv_workspace_bytes(B, K, V) > 16777216), or SV_ERR_HIP when the
+ * array's address cannot be obtained. */
+int sv_verify_batch_noalloc(const void* target_logits, const void* draft_logits, int dtype, int B,
+                            int K, int V, float temperature, const int32_t* draft_tokens,
+                            const int32_t* num_draft, const float* uniforms,
+                            const float* residual_uniform, int32_t* accepted_len,
+                            int32_t* committed, float* target_prob, float* draft_prob,
+                            void* stream);
+
 /* Greedy-mode verification ("Bringing DSpark to vLLM Metal": greedy serving whose output ids
  * equal target-only greedy decoding). g_i = argmax_v target_logits[b, i, v] compared on the
  * stored values, lowest index on ties. n = first i < k_b with x_i != g_i, else k_b.

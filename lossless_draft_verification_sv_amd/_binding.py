@@ -56,6 +56,9 @@ def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
         lib.sv_verify_batch.argtypes = [vp, vp, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp,
                                         vp, vp, vp, sz, vp]
         lib.sv_verify_batch.restype = i32
+        lib.sv_verify_batch_noalloc.argtypes = [vp, vp, i32, i32, i32, i32, f32, vp, vp, vp, vp,
+                                                vp, vp, vp, vp, vp]
+        lib.sv_verify_batch_noalloc.restype = i32
         lib.sv_verify_greedy.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
         lib.sv_verify_greedy.restype = i32
         i64 = ctypes.c_int64

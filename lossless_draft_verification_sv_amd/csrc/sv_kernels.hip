@@ -44,6 +44,7 @@
 
 #include <climits>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "sv.h"
@@ -1758,6 +1759,38 @@ int launch_greedy(const GreedyArgs& a, long groups, hipStream_t stream) {
   return launch_status("sv_verify_greedy");
 }
 
+// Scratch memory of sv_verify_batch_noalloc: a file-scope device array, one per GPU the library
+// runs on, held until the process ends. Host code never passes the array's name to a kernel (on
+// the host it is only a stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, once per device with that device current, and is kept here.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+constexpr int kMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) uint64_t scratch[kScratchBytes / 8];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SV_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(SV_ERR_UNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(SV_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") +
+                                  (e != hipSuccess ? hipGetErrorString(e) : "null address"));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SV_OK;
+}
+
 }  // namespace
 
 // Error reporting shared with the library's other source files (sv_internal.h).
@@ -1852,6 +1885,32 @@ int sv_verify_batch(const void* target_logits, const void* draft_logits, int dty
                : launch_sample<float, false, false>(a, groups, s);
   return vec ? launch_sample<uint16_t, true, false>(a, groups, s)
              : launch_sample<uint16_t, false, false>(a, groups, s);
+}
+
+int sv_verify_batch_noalloc(const void* target_logits, const void* draft_logits, int dtype, int B,
+                            int K, int V, float temperature, const int32_t* draft_tokens,
+                            const int32_t* num_draft, const float* uniforms,
+                            const float* residual_uniform, int32_t* accepted_len,
+                            int32_t* committed, float* target_prob, float* draft_prob,
+                            void* stream) {
+  g_last_error.clear();
+  const size_t need = sv_workspace_bytes(B, K, V);  // 0: a shape outside the limits
+  if (need == 0)  // sv_verify_batch reports which argument is invalid, before any GPU call
+    return sv_verify_batch(target_logits, draft_logits, dtype, B, K, V, temperature,
+                           draft_tokens, num_draft, uniforms, residual_uniform, accepted_len,
+                           committed, target_prob, draft_prob, nullptr, 0, stream);
+  if (need > kScratchBytes)
+    return fail(SV_ERR_UNSUPPORTED, "sv_verify_batch_noalloc: this batch needs " +
+                                        std::to_string(need) + " bytes of scratch, more than the " +
+                                        std::to_string(kScratchBytes) +
+                                        " the library holds per GPU; call sv_verify_batch with a "
+                                        "workspace instead");
+  void* ws = nullptr;
+  const int st = scratch_of_current_device(&ws);
+  if (st != SV_OK) return st;
+  return sv_verify_batch(target_logits, draft_logits, dtype, B, K, V, temperature, draft_tokens,
+                         num_draft, uniforms, residual_uniform, accepted_len, committed,
+                         target_prob, draft_prob, ws, need, stream);
 }
 
 int sv_verify_ragged(const void* target_logits, const void* draft_logits, int dtype, int B,

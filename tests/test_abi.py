@@ -268,3 +268,16 @@ def test_markov_workspace_holds_the_draw_decisions():
         Bl = min(B, 64)
         one_launch = Bl * (ntile + Bl) * 16 + Bl * 8 + Bl * 16
         assert lib.sv_markov_workspace_bytes(B, V) >= max(one_launch, B * ntile * 8)
+
+
+def test_noalloc_validates_before_any_gpu_call(lib):
+    """The allocation-free entry point rejects a batch whose scratch would exceed the 16 MiB it
+    holds per GPU, and invalid shapes, before it looks anything up on a device."""
+    need = sv.sv_workspace_bytes(4096, 64, 151936)
+    assert need > 16 << 20
+    st = lib.sv_verify_batch_noalloc(FAKE, FAKE, sv.SV_DTYPE_BF16, 4096, 64, 151936, 1.0, FAKE,
+                                     None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    assert st == sv.SV_ERR_UNSUPPORTED and "16777216" in sv.sv_last_error()
+    st = lib.sv_verify_batch_noalloc(FAKE, FAKE, sv.SV_DTYPE_BF16, 0, 8, 1000, 1.0, FAKE, None,
+                                     FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    assert st == sv.SV_ERR_INVALID_ARG
