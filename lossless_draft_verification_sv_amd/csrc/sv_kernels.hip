@@ -70,6 +70,7 @@ constexpr int kLaneRowChunks = 32;  // up to this many chunks per row, one lane 
 constexpr int kSpinLimit = 1 << 21;  // polls (about 1 us each) before a waiting group gives up
 constexpr int32_t kTimedOut = -2;    // accepted_len value reported by a group that gave up
 constexpr int kPollSleep = 2;        // s_sleep units (64 clocks each) between two polls
+constexpr int kMaxDevices = 64;      // devices the host-side caches keep an entry for
 
 // ---------------------------------------------------------------------------------------------
 // Work decomposition (host side, shared by the workspace query and the launches).
@@ -93,7 +94,10 @@ int chunks_for(long rows, long units, long target_groups, long min_units, int ma
 
 Plan make_plan(int B, int K, int V) {
   Plan p;
-  p.C = chunks_for((long)B * (2 * K + 1), V, 8192, 4096, kStageMax / (2 * K + 1));
+  // about 6144 row-stat groups: fewer, longer groups stream with less per-group overhead (each
+  // ends with a block reduction and a publish), more, shorter ones shorten the drain of the
+  // stream, and a chunk close to a whole number of rounds leaves a short tail loop
+  p.C = chunks_for((long)B * (2 * K + 1), V, 6144, 4096, kStageMax / (2 * K + 1));
   p.NT = (V + kTile - 1) / kTile;
   // About kDrawGroups draw groups in all, so that every one of them is resident once the
   // row-stat groups drain (more queue behind each other and delay the last requests' draws);
@@ -569,6 +573,7 @@ struct SampleArgs {
   const float* residual;
   float c32;  // log2(e) / temperature, rounded to fp32
   int C, C2, NT;
+  int L;               // draw groups of request b follow the rows of request b + L (grid order)
   uint32_t tag;        // this call's tag
   uint64_t* stats;
   uint64_t* gath;  // [B][K][2]
@@ -740,20 +745,16 @@ __device__ __forceinline__ void chunk_bounds(int G, int c, int C, int align, int
   g1 = c + 1 == C ? G : (int)((long)G * (c + 1) / C) & ~(align - 1);
 }
 
-// Row-stat group wg = (b * (2K+1) + slot) * C + c. Row slot s <= K is target row s, slot K+1+d
-// is draft row d. Unused rows (s > k_b, d >= k_b) return at once without a read.
+// Row-stat group (b, slot, c): chunk c of row slot `slot` of request b. Slot s <= K is target row
+// s, slot K+1+d is draft row d. Unused rows (s > k_b, d >= k_b) return at once without a read.
 // Publishes stats[b][s][c] = (o, sum) with sum = sum_v 2^(fma(z_v, c32, -o)), and, for target
 // slots i < k_b and draft slots i < k_b, the group whose chunk holds the draft token x_i
 // publishes its logit in gath[b][i][0] (target row i) or gath[b][i][1] (draft row i).
 template <typename T, bool VEC, bool GEN>
-__device__ void row_stat_group(const SampleArgs& a, long wg) {
+__device__ void row_stat_group(const SampleArgs& a, int b, int slot, int c) {
   constexpr int E = Rows<T, VEC>::E;
   const int K = a.K, V = a.V, C = a.C;
   const int NR = 2 * K + 1;
-  const int c = (int)(wg % C);
-  const long rs = wg / C;
-  const int slot = (int)(rs % NR);
-  const int b = (int)(rs / NR);
   const Req<T> q = request_of<T, GEN>(a, b);
   if (GEN && q.bad) return;
   const int k = q.k;
@@ -1252,12 +1253,11 @@ __device__ void greedy_request_finish(const SampleArgs& a, int b, int k, uint64_
   if (lane == 0) a.accepted_len[b] = n;
 }
 
-// Draw group j = b * C2 + c2; chunk c2 covers tiles [NT*c2/C2, NT*(c2+1)/C2).
+// Draw group (b, c2) of request b; chunk c2 covers tiles [NT*c2/C2, NT*(c2+1)/C2).
 template <typename T, bool VEC, bool GEN>
-__device__ void draw_group(const SampleArgs& a, long j) {
+__device__ void draw_group(const SampleArgs& a, int b, int c2) {
   constexpr int E = Rows<T, VEC>::E;
   const int K = a.K, V = a.V, C = a.C, C2 = a.C2, NT = a.NT;
-  const int b = (int)(j / C2), c2 = (int)(j % C2);
   const int NR = 2 * K + 1;
   const Req<T> q = request_of<T, GEN>(a, b);
   const int k = q.k;
@@ -1299,12 +1299,16 @@ __device__ void draw_group(const SampleArgs& a, long j) {
   const float uni = lane < k ? a.uniforms[(size_t)b * K + lane] : 0.0f;
   const bool want_x = xi >= 0 && xi < V;
 
-  // 1. Wait for every partial of the request and the logits at the draft tokens to carry this
-  //    call's tag; the words read in the last round are the data. Entries e < nent are
+  // 1. Wait for the partials the decision needs and the logits at the draft tokens to carry
+  //    this call's tag; the words read in the last round are the data. Entries e < nent are
   //    row-stat partials, e = row * C + chunk (staged chunk-major as offset bits, sum bits),
-  //    entries nent + i the two logits of draft token i.
+  //    entries nent + i the two logits of draft token i. The partials of target row k (row k
+  //    of the staging) are awaited only when an all-accepted block's token is drawn by tiles
+  //    (NS == 0): the segment draw needs only the row's segment partials, so the decision
+  //    does not wait for that row; its staged entries stay empty.
   const int nrow = 2 * k + 1, nent = nrow * C;  // nent <= kStageMax by the plan
   const int ntot = nent + k;
+  const bool want_row_k = a.NS == 0;
   bool late = false;
   for (int e0 = 0; e0 < ntot; e0 += kBlock * 4) {
     const uint64_t* p[4];
@@ -1313,7 +1317,7 @@ __device__ void draw_group(const SampleArgs& a, long j) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int e = e0 + u * kBlock + (int)threadIdx.x;
-      live[u] = e < ntot;
+      live[u] = e < ntot && (want_row_k || e / C != k || e >= nent);
       if (e < nent) {
         const int r_ = e / C, c = e % C;
         const int slot = r_ <= k ? r_ : K + 1 + (r_ - k - 1);
@@ -1328,7 +1332,8 @@ __device__ void draw_group(const SampleArgs& a, long j) {
     for (int u = 0; u < 4; ++u) {
       const int e = e0 + u * kBlock + (int)threadIdx.x;
       if (e < nent) {
-        stage[(e % C) * nrow + e / C] = ((uint64_t)payload(w0[u]) << 32) | payload(w1[u]);
+        stage[(e % C) * nrow + e / C] =
+            live[u] ? ((uint64_t)payload(w0[u]) << 32) | payload(w1[u]) : kEmptyStat;
       } else if (e < ntot) {
         s_zt[e - nent] = __uint_as_float(payload(w0[u]));
         s_zd[e - nent] = __uint_as_float(payload(w1[u]));
@@ -1438,17 +1443,21 @@ __device__ void draw_group(const SampleArgs& a, long j) {
 
   // 4'. Every draft kept: the token is drawn from p_n (n = k) by the request's first draw group
   //     alone, from the segment partials of its row-stat groups: await them, scale them to the
-  //     row's offset (exact), pick the segment holding r * Z (every wave, the same answer), and
-  //     wave 0 finds the token inside it. The staged partials are dead by now (every wave has its
-  //     normalisers), so the segment values reuse s_buf: fp64 values, then their fp32 offsets.
+  //     largest segment offset (exact), pick the segment holding r * Z (every wave, the same
+  //     answer), and wave 0 finds the token inside it. The draw needs no normaliser of the row:
+  //     r * Z and the running sums are on one scale. The staged partials are dead by now (every
+  //     wave has its normalisers), so the segment values reuse s_buf: fp64 values, then their
+  //     fp32 offsets.
   if (!resid && a.NS > 0) {
     if (c2 != 0) return;
     const int NS = a.NS;  // <= kSegMax
     double* vals = s_buf;
     float* offs = reinterpret_cast<float*>(s_buf + kSegMax);
+    __shared__ float s_omax[kWaves];
     const uint64_t* sg = a.seg + (size_t)b * a.NSmax * 2;
     __syncthreads();
     bool late3 = false;
+    float om = -FLT_MAX;
     for (int e0 = 0; e0 < NS; e0 += kBlock * 4) {
       const uint64_t* p[4];
       bool live[4];
@@ -1465,25 +1474,35 @@ __device__ void draw_group(const SampleArgs& a, long j) {
         const int e = e0 + u * kBlock + (int)threadIdx.x;
         if (e < NS) {
           const float os = __uint_as_float(payload(wo[u]));
-          const float d = fmaxf(os - w.oT, -2000.0f);  // <= 0: oT is the largest offset
-          vals[e] = ldexp((double)__uint_as_float(payload(ws[u])), (int)d);
+          vals[e] = (double)__uint_as_float(payload(ws[u]));
           offs[e] = os;
+          om = fmaxf(om, os);
         }
       }
     }
+    om = wave_max_f32(om);
+    if (lane == 0) s_omax[wave] = om;
     if (block_any(late3, s_late2)) {
       if (threadIdx.x == 0) a.accepted_len[b] = kTimedOut;
       return;
     }
+#pragma unroll
+    for (int w2 = 0; w2 < kWaves; ++w2) om = fmaxf(om, s_omax[w2]);
+    for (int e = threadIdx.x; e < NS; e += kBlock)
+      vals[e] = ldexp(vals[e], (int)fmaxf(offs[e] - om, -2000.0f));  // exponent <= 0
+    __syncthreads();
     const Pick pk = wave_pick(vals, NS, r, 0.0);
     if (pk.idx < 0) {  // no mass at all (non-finite logits): the tile draw over the whole row
-      const int y = full_row_draw<T, VEC>(rt, w, c32, G, NT, r, s_buf + kStageMax - kChunkTiles);
+      DrawParams wk = w;
+      wk.oT = om;
+      wk.iT = 1.0f;
+      const int y = full_row_draw<T, VEC>(rt, wk, c32, G, NT, r, s_buf + kStageMax - kChunkTiles);
       if (threadIdx.x == 0) a.committed[(size_t)b * (K + 1) + n] = y < 0 ? 0 : y;
       return;
     }
     if (wave != 0) return;
     const float os = offs[pk.idx];
-    const double rel = pk.found ? ldexp(pk.rel, (int)fmaxf(w.oT - os, 0.0f)) : INFINITY;
+    const double rel = pk.found ? ldexp(pk.rel, (int)fmaxf(om - os, 0.0f)) : INFINITY;
     const int y = segment_find<T, VEC>(rt, c32, os, G, pk.idx, rel);
     if (lane == 0) a.committed[(size_t)b * (K + 1) + n] = y < 0 ? 0 : y;
     return;
@@ -1559,25 +1578,65 @@ __device__ void draw_group(const SampleArgs& a, long j) {
   if (lane == 0) a.committed[(size_t)b * (K + 1) + n] = y < 0 ? 0 : y;
 }
 
-// Grid order: every row-stat group, then every draw group, so a draw group waits only on groups
-// dispatched before it (and on its siblings, next to it in the grid). Draw groups placed among
-// the row-stat groups measured slower: while one waits, it holds a slot the stream could use.
+// Grid order. Request by request, the (2K+1)*C row-stat groups of request j (slot by slot,
+// chunk by chunk), followed, once j >= L, by the C2 draw groups of request j - L; after the last
+// request, the draw groups of the last L requests. With a lag L of about the number of requests
+// whose row-stat groups are resident at once (the host sets it from the kernel's occupancy), a
+// request's draw groups are dispatched when its rows have mostly been streamed: they draw while
+// later requests stream, instead of all together after the last row. Every wait is on groups
+// earlier in the grid, which are dispatched first.
+struct SampleRole {
+  bool draw;
+  int b, slot, c;  // row-stat group: request, row slot, chunk; draw group: request, -, chunk
+};
+
+__device__ __forceinline__ SampleRole sample_role(const SampleArgs& a, long idx) {
+  const int K = a.K, C = a.C, L = a.L;
+  const long F = (2L * K + 1) * C;  // a request's row-stat groups
+  const long Q = a.C2;              // its draw groups
+  const long n1 = (long)L * F, n2 = (long)(a.B - L) * (F + Q);
+  SampleRole r;
+  long q;
+  if (idx < n1) {
+    r.b = (int)(idx / F);
+    q = idx % F;
+    r.draw = false;
+  } else if (idx < n1 + n2) {
+    const long i = idx - n1;
+    q = i % (F + Q);
+    r.draw = q >= F;
+    r.b = (int)(L + i / (F + Q) - (r.draw ? L : 0));
+    if (r.draw) q -= F;
+  } else {
+    const long i = idx - n1 - n2;
+    r.b = (int)(a.B - L + i / Q);
+    q = i % Q;
+    r.draw = true;
+  }
+  if (r.draw) {
+    r.slot = 0;
+    r.c = (int)q;
+  } else {
+    r.slot = (int)(q / C);
+    r.c = (int)(q % C);
+  }
+  return r;
+}
+
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kBlock) void sv_verify_sample(SampleArgs a) {
-  const long wg = blockIdx.x;
-  const long n_stat = (long)a.B * (2 * a.K + 1) * a.C;
-  if (wg < n_stat) row_stat_group<T, VEC, false>(a, wg);
-  else draw_group<T, VEC, false>(a, wg - n_stat);
+  const SampleRole r = sample_role(a, (long)blockIdx.x);
+  if (!r.draw) row_stat_group<T, VEC, false>(a, r.b, r.slot, r.c);
+  else draw_group<T, VEC, false>(a, r.b, r.c);
 }
 
 // Flattened, mixed calls: the same grid and groups, each request read through its own rows and
 // temperature.
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(VEC ? 6 : 1))) void sv_verify_ragged_kernel(SampleArgs a) {
-  const long wg = blockIdx.x;
-  const long n_stat = (long)a.B * (2 * a.K + 1) * a.C;
-  if (wg < n_stat) row_stat_group<T, VEC, true>(a, wg);
-  else draw_group<T, VEC, true>(a, wg - n_stat);
+  const SampleRole r = sample_role(a, (long)blockIdx.x);
+  if (!r.draw) row_stat_group<T, VEC, true>(a, r.b, r.slot, r.c);
+  else draw_group<T, VEC, true>(a, r.b, r.c);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1741,8 +1800,38 @@ int segments_per_row(int V, int dtype, bool vec, const Plan& p) {
   return ns <= p.NSmax ? (int)ns : 0;
 }
 
+// Work-groups of `kernel` resident at once on the current device (cached per device).
+long resident_groups(const void* kernel, long* cache) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 1536;
+  if (cache[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0) != hipSuccess ||
+        per_cu < 1)
+      per_cu = 6;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+      cus = 256;
+    cache[dev] = (long)per_cu * cus;
+  }
+  return cache[dev];
+}
+
 template <typename T, bool VEC, bool GEN>
-int launch_sample(const SampleArgs& a, long groups, hipStream_t stream) {
+int launch_sample(const SampleArgs& args, long groups, hipStream_t stream) {
+  const void* kernel = GEN ? reinterpret_cast<const void*>(&sv_verify_ragged_kernel<T, VEC>)
+                           : reinterpret_cast<const void*>(&sv_verify_sample<T, VEC>);
+  static long cache[kMaxDevices] = {};
+  SampleArgs a = args;
+  // The lag: about the number of requests whose row-stat groups are resident at once, plus two.
+  // In ragged batches (verify lengths per request) the rows past k_b are skipped, so the host
+  // cannot tell how many requests stream at once; a lag too short makes draw groups wait for
+  // their rows while holding slots the stream needs, which measured slower than no lag at all,
+  // so there every draw group follows the last row-stat group (L = B).
+  const long per_request = (2L * a.K + 1) * a.C;
+  long L = (resident_groups(kernel, cache) + per_request - 1) / per_request + 2;
+  if (GEN || a.num_draft != nullptr || L > a.B) L = a.B;
+  a.L = (int)L;
   if (GEN)
     hipLaunchKernelGGL((sv_verify_ragged_kernel<T, VEC>), dim3((unsigned)groups), dim3(kBlock),
                        0, stream, a);
@@ -1764,7 +1853,6 @@ int launch_greedy(const GreedyArgs& a, long groups, hipStream_t stream) {
 // the host it is only a stand-in for the symbol): the device address comes from
 // hipGetSymbolAddress, once per device with that device current, and is kept here.
 constexpr size_t kScratchBytes = (size_t)16 << 20;
-constexpr int kMaxDevices = 64;
 }  // namespace
 
 static __device__ __align__(256) uint64_t scratch[kScratchBytes / 8];
@@ -1837,6 +1925,7 @@ int sv_verify_batch(const void* target_logits, const void* draft_logits, int dty
   const double c64 = 1.4426950408889634074 / (double)temperature;  // log2(e) / temperature
   if (!(c64 >= (double)FLT_MIN && c64 <= 2097152.0))
     return fail(SV_ERR_INVALID_ARG, "temperature out of range");
+  const bool vec = rows_vectorisable(target_logits, draft_logits, dtype, V);
   const Plan p = make_plan(B, K, V);
   if (!plan_supported(p)) return fail(SV_ERR_UNSUPPORTED, "vocabulary too large");
   const Layout L = make_layout(B, K, V, p);
@@ -1878,7 +1967,6 @@ int sv_verify_batch(const void* target_logits, const void* draft_logits, int dty
   a.t_start = a.d_start = nullptr;
   a.n_trows = a.n_drows = 0;
   a.temps = nullptr;
-  const bool vec = rows_vectorisable(target_logits, draft_logits, dtype, V);
   a.NS = segments_per_row(V, dtype, vec, p);
   if (dtype == SV_DTYPE_F32)
     return vec ? launch_sample<float, true, false>(a, groups, s)
