@@ -276,8 +276,11 @@ def bench_schedule(args):
     ds = torch.empty(B, dtype=torch.int32, device=dev)
     summ = torch.empty(2, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    nbytes = int(lib.sv_schedule_workspace_bytes(B, K))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
     argv = (c_d.data_ptr(), B, K, t_d.data_ptr(), tab.shape[0], 0.5, out.data_ptr(),
-            ts.data_ptr(), ds.data_ptr(), summ.data_ptr(), stream.cuda_stream)
+            ts.data_ptr(), ds.data_ptr(), summ.data_ptr(), ws.data_ptr(), nbytes,
+            stream.cuda_stream)
     for _ in range(args.warmup):
         assert lib.sv_schedule_prefix(*argv) == 0
     torch.cuda.synchronize()

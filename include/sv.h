@@ -118,8 +118,8 @@ int sv_verify_batch(const void* target_logits, const void* draft_logits, int dty
  * undefined results; serialise them. The array is zero-filled on the stream before its first use on
  * each device (and after a wrap of the call counter), as a workspace is.
  * Returns what sv_verify_batch returns, or SV_ERR_UNSUPPORTED (nothing launched) when the batch
- * needs more than 16 MiB of scratch (sv_workspace_bytes(B, K, V) > 16777216), or SV_ERR_HIP when the
- * array's address cannot be obtained. */
+ * needs more than 16 MiB of scratch (sv_workspace_bytes(B, K, V) > 16777216), or SV_ERR_HIP when
+ * the array's address cannot be obtained. */
 int sv_verify_batch_noalloc(const void* target_logits, const void* draft_logits, int dtype, int B,
                             int K, int V, float temperature, const int32_t* draft_tokens,
                             const int32_t* num_draft, const float* uniforms,
@@ -200,13 +200,25 @@ int sv_verify_ragged(const void* target_logits, const void* draft_logits, int dt
  *  target_row_start  [B] int32 out or NULL: exclusive sums of k_b + 1 (flattened target rows)
  *  draft_row_start   [B] int32 out or NULL: exclusive sums of k_b (flattened draft rows)
  *  summary           [2] float out or NULL: N chosen, and its expected tokens per unit time
- *                    (0, 0 in threshold mode)
- *  Limits: 1 <= K <= 64, B*K <= 4096. One work-group; asynchronous on `stream`.
- * Returns SV_OK, SV_ERR_INVALID_ARG (nothing launched) or SV_ERR_HIP.
+ *                    (0, 0 in threshold mode; -1, 0 if the finishing work-group's bounded wait
+ *                    for the ranking work-groups ran out, which leaves every k_b = 0)
+ *  workspace         hardware-aware mode: device memory of at least
+ *                    sv_schedule_workspace_bytes(B, K) bytes, 8-byte aligned (the ranking
+ *                    work-groups' results, tagged words as for the verify calls; reusable
+ *                    across calls and shapes on one stream, shared with the verify calls'
+ *                    workspaces). Threshold mode: may be NULL.
+ *  Limits: 1 <= K <= 64, B*K <= 4096. Hardware-aware mode: ceil(B*K / 8) ranking work-groups
+ *  and one finishing work-group, last in the grid (no token order is
+ *  materialised: each token's rank and the survival sum before it come from a binary search in
+ *  every request's block, whose survivals never increase); threshold mode: one work-group.
+ *  Asynchronous on `stream`.
+ * Returns SV_OK, SV_ERR_INVALID_ARG or SV_ERR_WORKSPACE (nothing launched) or SV_ERR_HIP.
  */
+size_t sv_schedule_workspace_bytes(int B, int K);
 int sv_schedule_prefix(const float* confidence, int B, int K, const float* step_time, int T,
                        float threshold, int32_t* num_draft, int32_t* target_row_start,
-                       int32_t* draft_row_start, float* summary, void* stream);
+                       int32_t* draft_row_start, float* summary, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 /* Markov-head correction of a parallel draft block ("Accelerating Large-Model Inference ...",
  * section 3, Markov Head; DSpark paper review 4.1): left to right over positions k = 0..K-1,

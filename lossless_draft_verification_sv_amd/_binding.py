@@ -65,8 +65,11 @@ def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
         lib.sv_verify_ragged.argtypes = [vp, vp, i32, i32, i32, i32, i64, i64, vp, vp, vp, vp,
                                          vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.sv_verify_ragged.restype = i32
-        lib.sv_schedule_prefix.argtypes = [vp, i32, i32, vp, i32, f32, vp, vp, vp, vp, vp]
+        lib.sv_schedule_prefix.argtypes = [vp, i32, i32, vp, i32, f32, vp, vp, vp, vp, vp, sz,
+                                           vp]
         lib.sv_schedule_prefix.restype = i32
+        lib.sv_schedule_workspace_bytes.argtypes = [i32, i32]
+        lib.sv_schedule_workspace_bytes.restype = sz
         lib.sv_markov_workspace_bytes.argtypes = [i32, i32]
         lib.sv_markov_workspace_bytes.restype = sz
         lib.sv_markov_draft.argtypes = [vp, i32, i32, i32, i32, vp, vp, i32, vp, vp, vp, vp, sz,
@@ -303,8 +306,13 @@ def sv_schedule_prefix(confidence: torch.Tensor, step_time: Optional[torch.Tenso
     ds = torch.empty(B, dtype=torch.int32, device=dev)
     summ = torch.empty(2, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
+    ws, nbytes = None, 0
+    if step_time is not None:
+        nbytes = int(lib.sv_schedule_workspace_bytes(B, K))
+        ws = _workspace(dev, stream, nbytes)
     _check(lib.sv_schedule_prefix(_ptr(confidence), B, K, _ptr(step_time), T, float(threshold),
-                                  _ptr(num), _ptr(ts), _ptr(ds), _ptr(summ), stream))
+                                  _ptr(num), _ptr(ts), _ptr(ds), _ptr(summ), _ptr(ws), nbytes,
+                                  stream))
     return ScheduleOutput(num, ts, ds, summ)
 
 

@@ -199,10 +199,30 @@ def test_read_probe_rejects_invalid_arguments(lib):
                                 dict(T=16), dict(table=None, threshold=float("nan"))])
 def test_schedule_rejects_invalid_arguments(lib, kw):
     args = dict(conf=FAKE, B=4, K=4, table=FAKE, T=4 + 16 + 1, threshold=0.5, num=FAKE,
-                ts=None, ds=None, summary=None, stream=None)
+                ts=None, ds=None, summary=None, ws=WS, ws_bytes=1 << 20, stream=None)
     args.update(kw)
     assert lib.sv_schedule_prefix(*args.values()) == sv.SV_ERR_INVALID_ARG
     assert sv.sv_last_error() != ""
+
+
+@pytest.mark.parametrize("kw", [dict(ws=None), dict(ws=WS + 4), dict(ws_bytes=8)])
+def test_schedule_checks_its_workspace_in_hardware_aware_mode(lib, kw):
+    args = dict(conf=FAKE, B=4, K=4, table=FAKE, T=4 + 16 + 1, threshold=0.5, num=FAKE,
+                ts=None, ds=None, summary=None, ws=WS, ws_bytes=1 << 20, stream=None)
+    args.update(kw)
+    assert lib.sv_schedule_prefix(*args.values()) == sv.SV_ERR_WORKSPACE
+    assert "workspace" in sv.sv_last_error()
+
+
+def test_schedule_workspace_size(lib):
+    # ceil(B*K / 8) ranking work-groups, three 8-byte words each, rounded up to 256 bytes
+    assert lib.sv_schedule_workspace_bytes(256, 16) == 512 * 24
+    assert lib.sv_schedule_workspace_bytes(1, 1) == 256
+    assert lib.sv_schedule_workspace_bytes(4096, 1) == 512 * 24
+    assert lib.sv_schedule_workspace_bytes(3, 5) == 256
+    assert lib.sv_schedule_workspace_bytes(0, 4) == 0
+    assert lib.sv_schedule_workspace_bytes(4, 65) == 0
+    assert lib.sv_schedule_workspace_bytes(4097, 1) == 0
 
 
 @pytest.mark.parametrize("kw,status", [
