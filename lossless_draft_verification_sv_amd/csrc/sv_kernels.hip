@@ -934,13 +934,11 @@ __device__ __forceinline__ void merge_row_lanes(float& O, double& S, int RL) {
 // the lanes (fp64 lane sums in element order, then a wave prefix sum); the first lane whose
 // prefix passes the target walks its own elements.
 template <typename T, bool VEC, bool RESID>
-__device__ int tile_find(const T* rt, const T* rd, const DrawParams& w, float c32, int G, int t,
-                         double target) {
+__device__ int tile_find_loaded(const TileRows<T, VEC, RESID>& tr, const DrawParams& w, float c32,
+                                int t, double target) {
   using TR = TileRows<T, VEC, RESID>;
   constexpr int E = TR::E;
   const int lane = threadIdx.x & 63;
-  TR tr;
-  tr.load(rt, rd, t, G, lane);
   double base = 0.0;
   int last_pos = -1;
 #pragma unroll
@@ -974,6 +972,14 @@ __device__ int tile_find(const T* rt, const T* rd, const DrawParams& w, float c3
     base += lane_f64(incl, 63);
   }
   return wave_max_i32(last_pos);
+}
+
+template <typename T, bool VEC, bool RESID>
+__device__ int tile_find(const T* rt, const T* rd, const DrawParams& w, float c32, int G, int t,
+                         double target) {
+  TileRows<T, VEC, RESID> tr;
+  tr.load(rt, rd, t, G, threadIdx.x & 63);
+  return tile_find_loaded<T, VEC, RESID>(tr, w, c32, t, target);
 }
 
 // Per-tile weight sums of tiles [t0, t1) by the 4 waves of the group, kTileUnroll tiles per wave
@@ -1516,8 +1522,36 @@ __device__ void draw_group(const SampleArgs& a, int b, int c2) {
   double* ctot = tsum + kChunkTiles;                         // [kMaxC2]
   if (nent > kStageMax - kChunkTiles - kMaxC2) __syncthreads();
   const int t0 = (int)((long)NT * c2 / C2), t1 = (int)((long)NT * (c2 + 1) / C2);
-  if (resid) tile_sums<T, VEC, true>(rt, rd, w, c32, G, t0, t1, tsum);
-  else tile_sums<T, VEC, false>(rt, rd, w, c32, G, t0, t1, tsum);
+  // A residual chunk of one round keeps its tiles in registers (tile t0 + wave + u * kWaves in
+  // held[u]): the wave that loaded the chosen tile finds the token in it without reading it again.
+  // Only 16-byte bf16 rows of the padded call: there a tile takes 8 registers per lane, and the
+  // other kernels' register budgets have no room for it.
+  constexpr bool kMayHold = !GEN && VEC && sizeof(T) == 2;
+  TileRows<T, VEC, true> held[kMayHold ? kTileUnroll : 1];
+  const bool hold = kMayHold && resid && t1 - t0 <= kWaves * kTileUnroll;
+  if constexpr (kMayHold) {
+    if (hold) {
+#pragma unroll
+      for (int u = 0; u < kTileUnroll; ++u) {
+        const int tu = t0 + wave + u * kWaves;
+        if (tu < t1) held[u].load(rt, rd, tu, G, lane);
+      }
+#pragma unroll
+      for (int u = 0; u < kTileUnroll; ++u) {
+        const int tu = t0 + wave + u * kWaves;
+        if (tu < t1) {
+          const double sum = wave_sum_f64(held[u].lane_sum(w, c32));
+          if (lane == 0) tsum[tu - t0] = sum;
+        }
+      }
+    }
+  }
+  if (hold) {
+  } else if (resid) {
+    tile_sums<T, VEC, true>(rt, rd, w, c32, G, t0, t1, tsum);
+  } else {
+    tile_sums<T, VEC, false>(rt, rd, w, c32, G, t0, t1, tsum);
+  }
   __syncthreads();
   uint64_t* ct = a.ctot + (size_t)b * C2 * 2;
   if (wave == 0) {
@@ -1565,15 +1599,30 @@ __device__ void draw_group(const SampleArgs& a, int b, int c2) {
     if (threadIdx.x == 0) a.committed[(size_t)b * (K + 1) + n] = y < 0 ? 0 : y;
     return;
   }
-  if (pc.idx != c2 || wave != 0) return;
+  if (pc.idx != c2) return;
 
-  // 7. This group holds r * Z: wave 0 picks the tile inside the chunk, then the token inside it.
+  // 7. This group holds r * Z: every wave picks the tile inside the chunk (the same answer); the
+  //    wave that holds it (wave 0 when the tiles were not held) finds the token inside it.
   const Pick pt = wave_pick(tsum, t1 - t0, -1.0, pc.rel);
+  const int finder = hold && pt.idx >= 0 ? pt.idx % kWaves : 0;
+  if (wave != finder) return;
   int y = -1;
   if (pt.idx >= 0) {
     const double rel = pc.found ? pt.rel : INFINITY;
-    y = resid ? tile_find<T, VEC, true>(rt, rd, w, c32, G, t0 + pt.idx, rel)
-              : tile_find<T, VEC, false>(rt, rd, w, c32, G, t0 + pt.idx, rel);
+    if constexpr (kMayHold) {
+      if (hold) {
+        const int sel = pt.idx / kWaves;  // wave-uniform; copied out without indexing registers
+        TileRows<T, VEC, true> tr = held[0];
+#pragma unroll
+        for (int u = 1; u < kTileUnroll; ++u)
+          if (sel == u) tr = held[u];
+        y = tile_find_loaded<T, VEC, true>(tr, w, c32, t0 + pt.idx, rel);
+      }
+    }
+    if (!hold) {
+      y = resid ? tile_find<T, VEC, true>(rt, rd, w, c32, G, t0 + pt.idx, rel)
+                : tile_find<T, VEC, false>(rt, rd, w, c32, G, t0 + pt.idx, rel);
+    }
   }
   if (lane == 0) a.committed[(size_t)b * (K + 1) + n] = y < 0 ? 0 : y;
 }
@@ -1590,26 +1639,29 @@ struct SampleRole {
   int b, slot, c;  // row-stat group: request, row slot, chunk; draw group: request, -, chunk
 };
 
-__device__ __forceinline__ SampleRole sample_role(const SampleArgs& a, long idx) {
-  const int K = a.K, C = a.C, L = a.L;
-  const long F = (2L * K + 1) * C;  // a request's row-stat groups
-  const long Q = a.C2;              // its draw groups
-  const long n1 = (long)L * F, n2 = (long)(a.B - L) * (F + Q);
+// (32-bit arithmetic: the host keeps a grid below 2^24 groups, and 64-bit divisions at every
+// group's start measured 0.2-0.3 us slower on the batched call.)
+__device__ __forceinline__ SampleRole sample_role(const SampleArgs& a, long idx_l) {
+  const uint32_t K = a.K, C = a.C, L = a.L;
+  const uint32_t F = (2u * K + 1u) * C;
+  const uint32_t Q = a.C2;
+  const uint32_t n1 = L * F, n2 = ((uint32_t)a.B - L) * (F + Q);
+  const uint32_t idx = (uint32_t)idx_l;
   SampleRole r;
-  long q;
+  uint32_t q;
   if (idx < n1) {
     r.b = (int)(idx / F);
     q = idx % F;
     r.draw = false;
   } else if (idx < n1 + n2) {
-    const long i = idx - n1;
+    const uint32_t i = idx - n1;
     q = i % (F + Q);
     r.draw = q >= F;
     r.b = (int)(L + i / (F + Q) - (r.draw ? L : 0));
     if (r.draw) q -= F;
   } else {
-    const long i = idx - n1 - n2;
-    r.b = (int)(a.B - L + i / Q);
+    const uint32_t i = idx - n1 - n2;
+    r.b = (int)((uint32_t)a.B - L + i / Q);
     q = i % Q;
     r.draw = true;
   }
