@@ -1191,10 +1191,13 @@ __device__ __forceinline__ void row_norm(const uint64_t* st, int C, int stride, 
 
 // 2^a for a <= 0 in fp64, to about fp32's relative accuracy: an exact split into the integer
 // part and the fraction, which goes through v_exp_f32 (relative error ~1e-7).
+// Exponents below -1100 (a logit of -inf among them: probability 0) give 0, as 2^a rounds to 0
+// in fp64 there; taking the split of -inf itself would give NaN.
 __device__ __forceinline__ double exp2_split(double a) {
+  a = fmax(a, -1100.0);
   const double fl = floor(a);
   const float fr = (float)(a - fl);  // [0, 1]
-  return ldexp((double)__builtin_amdgcn_exp2f(fr), (int)fmax(fl, -2000.0));
+  return ldexp((double)__builtin_amdgcn_exp2f(fr), (int)fl);
 }
 
 // Greedy request inside a mixed call, by its chunk-0 draw group: waits for the argmax partials of

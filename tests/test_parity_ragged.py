@@ -86,6 +86,22 @@ def test_mixed_flat_small(B, K, V, dtype, seed):
     check_ragged_parity(w.name, flatten(inp, order))
 
 
+@pytest.mark.parametrize("V,dtype", [(16400, "bf16"), (4099, "f32")])
+def test_mixed_flat_masked_vocabulary(V, dtype):
+    """Most entries of every row at -inf (a filtered vocabulary), target and draft masks drawn
+    independently, in a mixed batch: greedy and sampling requests, vector and scalar rows."""
+    w = MIXED.replace(name=f"mixed_masked_V{V}_{dtype}", B=12, K=6, V=V, dtype=dtype,
+                      seed=4200 + V % 13)
+    inp = generate(w)
+    rng = np.random.default_rng(4300 + V)
+    neg_inf = np.uint16(0xFF80) if dtype == "bf16" else np.float32(-np.inf)
+    for rows in (inp.target, inp.draft):
+        keep = rng.random(rows.shape) < 0.4
+        keep[..., rng.integers(0, V)] = True  # every row keeps at least one finite entry
+        rows[~keep] = neg_inf
+    check_ragged_parity(w.name, flatten(inp, rng.permutation(w.B)))
+
+
 def test_flat_equals_padded_bitwise():
     """All-sampling ragged batch: flattened and padded calls give identical outputs."""
     w = HEAVY.replace(name="heavy_small", B=24, K=8, V=40000, seed=4101)

@@ -117,6 +117,31 @@ def test_misaligned_rows_take_the_scalar_path():
     assert np.max(np.abs(out.target_prob.cpu().numpy() - ref.target_prob)) <= 1e-5
 
 
+@pytest.mark.parametrize("V,dtype", [(20000, "f32"), (20000, "bf16"), (4099, "f32"),
+                                     (4099, "bf16")])
+def test_masked_vocabulary(V, dtype):
+    """Rows with most entries at -inf (a filtered vocabulary: probability 0), the target and
+    draft masks drawn independently, so that draft tokens can fall where p or q is 0; one target
+    row and one draft row keep a single finite entry. Vector and scalar row paths."""
+    inp = generate(BATCHED.replace(name=f"masked_V{V}_{dtype}", B=6, K=4, V=V, dtype=dtype,
+                                   seed=81 + V % 11))
+    rng = np.random.default_rng(83 + V)
+    neg_inf = np.uint16(0xFF80) if dtype == "bf16" else np.float32(-np.inf)
+    for rows in (inp.target, inp.draft):
+        keep = rng.random(rows.shape) < 0.4
+        keep[..., rng.integers(0, V)] = True  # every row keeps at least one finite entry
+        rows[~keep] = neg_inf
+    def value(x):
+        v = np.array([x], dtype=np.float32)
+        return to_bf16_bits(v)[0] if dtype == "bf16" else v[0]
+
+    inp.target[0, 0, :] = neg_inf
+    inp.target[0, 0, int(rng.integers(0, V))] = value(1.5)
+    inp.draft[1, 1, :] = neg_inf
+    inp.draft[1, 1, inp.tokens[1, 1]] = value(2.0)
+    _check(inp)
+
+
 @pytest.mark.parametrize("tau", [0.05, 20.0])
 def test_extreme_temperatures(tau):
     w = TINY.replace(name=f"temperature_{tau}", B=6, K=4, V=8000, dtype="bf16",
