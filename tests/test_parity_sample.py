@@ -120,26 +120,38 @@ def test_misaligned_rows_take_the_scalar_path():
 @pytest.mark.parametrize("V,dtype", [(20000, "f32"), (20000, "bf16"), (4099, "f32"),
                                      (4099, "bf16")])
 def test_masked_vocabulary(V, dtype):
-    """Rows with most entries at -inf (a filtered vocabulary: probability 0), the target and
-    draft masks drawn independently, so that draft tokens can fall where p or q is 0; one target
-    row and one draft row keep a single finite entry. Vector and scalar row paths."""
+    """Rows with most entries at -inf (a filtered vocabulary: probability 0). Odd requests draw
+    the target and draft masks independently, so that draft tokens can fall where p or q is 0;
+    even requests (identical target and draft rows) share one mask, keep every draft and draw
+    the bonus token from a masked row. One target row and one draft row keep a single finite
+    entry (p, then q, a point mass). Vector and scalar row paths."""
     inp = generate(BATCHED.replace(name=f"masked_V{V}_{dtype}", B=6, K=4, V=V, dtype=dtype,
                                    seed=81 + V % 11))
     rng = np.random.default_rng(83 + V)
     neg_inf = np.uint16(0xFF80) if dtype == "bf16" else np.float32(-np.inf)
-    for rows in (inp.target, inp.draft):
-        keep = rng.random(rows.shape) < 0.4
-        keep[..., rng.integers(0, V)] = True  # every row keeps at least one finite entry
-        rows[~keep] = neg_inf
+    keep_t = rng.random(inp.target.shape) < 0.4
+    keep_d = rng.random(inp.draft.shape) < 0.4
+    K = inp.workload.K
+    for b in range(0, inp.workload.B, 2):
+        keep_t[b, np.arange(K), inp.tokens[b]] = True  # the drafted tokens keep their mass
+    keep_t[..., rng.integers(0, V)] = True  # every row keeps at least one finite entry
+    keep_d[1::2, :, rng.integers(0, V)] = True
+    keep_d[0::2] = keep_t[0::2, :-1]
+    inp.target[~keep_t] = neg_inf
+    inp.draft[~keep_d] = neg_inf
+
     def value(x):
         v = np.array([x], dtype=np.float32)
         return to_bf16_bits(v)[0] if dtype == "bf16" else v[0]
 
-    inp.target[0, 0, :] = neg_inf
-    inp.target[0, 0, int(rng.integers(0, V))] = value(1.5)
-    inp.draft[1, 1, :] = neg_inf
-    inp.draft[1, 1, inp.tokens[1, 1]] = value(2.0)
+    inp.target[1, 0, :] = neg_inf
+    inp.target[1, 0, int(rng.integers(0, V))] = value(1.5)
+    inp.draft[5, 0, :] = neg_inf  # q is a point mass at the drafted token
+    inp.draft[5, 0, inp.tokens[5, 0]] = value(2.0)
     _check(inp)
+    acc, _, _, _ = run_sample(inp.target, inp.draft, inp.tokens, inp.uniforms, inp.residual,
+                              inp.workload.temperature)
+    assert np.all(acc[0::2] == K)  # identical masked rows: every draft kept
 
 
 @pytest.mark.parametrize("tau", [0.05, 20.0])
