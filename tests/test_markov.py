@@ -121,6 +121,22 @@ def test_markov_parity(dtype, B, K, V, R):
     check_batch(f"{dtype} B{B} K{K} V{V} R{R}", base, dtype, left, right, anchor)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_markov_masked_vocabulary(dtype):
+    """Base rows with most entries at -inf (a filtered vocabulary): the bias cannot lift them,
+    so every token is one of the row's finite entries; two request blocks."""
+    B, K, V, R = 70, 4, 1000, 64
+    base = workloads.markov_base(B, K, V, dtype, seed=91)
+    left, right = workloads.markov_factors(V, R, seed=92)
+    rng = np.random.default_rng(93)
+    keep = rng.random(base.shape) < 0.3
+    keep[..., rng.integers(0, V)] = True
+    base[~keep] = np.uint16(0xFF80) if dtype == "bf16" else np.float32(-np.inf)
+    anchor = rng.integers(0, V, size=B).astype(np.int32)
+    tok, _ = check_batch(f"masked {dtype}", base, dtype, left, right, anchor)
+    assert np.all(keep[np.arange(B)[:, None], np.arange(K)[None, :], tok])
+
+
 def test_markov_sixty_four_positions():
     """K = 64: every hand-off between positions of the one-launch form, 64 of them in one call,
     and a second call on the same workspace (fresh call stamps)."""
