@@ -26,6 +26,18 @@ def device():
     return torch.device("cuda:0")
 
 
+def abs_err(got, ref) -> np.ndarray:
+    """|got - ref| elementwise, with equal infinities and NaN on both sides counted as no error
+    and a NaN on one side only as an infinite one (so that it never passes a tolerance check)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    with np.errstate(invalid="ignore"):
+        err = np.abs(got - ref)
+    err[((got == ref) & np.isinf(ref)) | (np.isnan(got) & np.isnan(ref))] = 0.0
+    err[np.isnan(err)] = np.inf
+    return err
+
+
 def to_dev(a: np.ndarray, dtype: str = None) -> torch.Tensor:
     if a is None:
         return None

@@ -21,7 +21,7 @@ import torch  # noqa: E402
 import lossless_draft_verification_sv_amd as sv  # noqa: E402
 import oracle  # noqa: E402
 import workloads  # noqa: E402
-from tests.gpu_util import say, to_dev  # noqa: E402
+from tests.gpu_util import abs_err, say, to_dev  # noqa: E402
 
 HERE = os.path.dirname(__file__)
 
@@ -49,7 +49,7 @@ def check_request(name, b, base_b, dtype, left, right, anchor_b, tok_b, logits_b
     K = ref_tok.shape[0]
     for k in range(K):
         if logits_b is not None:
-            err = np.abs(logits_b[k] - ref_z[k])
+            err = abs_err(logits_b[k], ref_z[k])
             bad = np.nonzero(err > logit_tol(ref_z[k], dtype))[0]
             assert bad.size == 0, (name, b, k, bad[:5], logits_b[k][bad[:5]], ref_z[k][bad[:5]])
         if gaps[k] < oracle.AMBIGUOUS_GAP:

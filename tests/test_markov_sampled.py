@@ -22,7 +22,7 @@ import torch  # noqa: E402
 import lossless_draft_verification_sv_amd as sv  # noqa: E402
 import oracle  # noqa: E402
 import workloads  # noqa: E402
-from tests.gpu_util import say, to_dev  # noqa: E402
+from tests.gpu_util import abs_err, say, to_dev  # noqa: E402
 
 HERE = os.path.dirname(__file__)
 PEAKED = 14.0  # markov_base lead of a sampling drafter's rows
@@ -56,7 +56,7 @@ def check_batch(name, base, dtype, left, right, tau, u, anchor, requests=None):
         a = -1 if anchor is None else int(anchor[b])
         ref_tok, ref_z, amb = oracle.markov_sampled_request(base[b], dtype, left, right, a,
                                                             float(tau[b]), u[b], choose=tok[b])
-        err = np.abs(logits[b] - ref_z)
+        err = abs_err(logits[b], ref_z)
         bad = np.argwhere(err > logit_bound(ref_z, dtype))
         assert bad.size == 0, (name, b, bad[:5], float(err.max()))
         assert np.array_equal(tok[b], ref_tok), (name, b, float(tau[b]), u[b], tok[b], ref_tok,

@@ -19,7 +19,7 @@ import torch  # noqa: E402
 import lossless_draft_verification_sv_amd as sv  # noqa: E402
 import oracle  # noqa: E402
 import workloads  # noqa: E402
-from tests.gpu_util import say, to_dev  # noqa: E402
+from tests.gpu_util import abs_err, say, to_dev  # noqa: E402
 
 HERE = os.path.dirname(__file__)
 
@@ -43,7 +43,7 @@ def check(name, base, dtype, left, right, kc, anchor, requests=None):
         rt, rc, rz, gaps = oracle.markov_topk_request(base[b], dtype, left, right, a, kc)
         for k in range(K):
             assert np.array_equal(cand[b, k], rc[k]), (name, b, k, cand[b, k][:8], rc[k][:8])
-            err = np.abs(z[b, k] - rz[k])
+            err = abs_err(z[b, k], rz[k])
             tol = 2e-5 + 1e-6 * np.abs(rz[k])
             assert np.all(err <= tol), (name, b, k, float(err.max()))
             if gaps[k] < oracle.AMBIGUOUS_GAP:
