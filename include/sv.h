@@ -115,8 +115,10 @@ int sv_verify_batch(const void* target_logits, const void* draft_logits, int dty
  * hipMalloc, hipFree or allocating library routine is called. The call runs on the current device
  * (`stream` must belong to it). Every call on one GPU shares that GPU's array, which keeps the last
  * call's words: calls that can overlap on one GPU (two streams, two host threads) race and give
- * undefined results; serialise them. The array is zero-filled on the stream before its first use on
- * each device (and after a wrap of the call counter), as a workspace is.
+ * undefined results; serialise them. Each call first zero-fills the part of the array it uses (a
+ * kernel on `stream`, no memset) and its work-groups hand values to each other under one fixed
+ * tag, so nothing depends on host state that changes from call to call: a call captured into a
+ * HIP graph gives correct results on every replay (replays, like calls, must not overlap).
  * Returns what sv_verify_batch returns, or SV_ERR_UNSUPPORTED (nothing launched) when the batch
  * needs more than 16 MiB of scratch (sv_workspace_bytes(B, K, V) > 16777216), or SV_ERR_HIP when
  * the array's address cannot be obtained. */

@@ -25,6 +25,11 @@ __attribute__((visibility("hidden"))) int sv_internal_call_tags(uint32_t step, v
                                                                 size_t bytes, hipStream_t s,
                                                                 uint32_t* tag);
 
+// Enqueues a zero fill of [ws, ws + bytes) on stream s (a kernel, no memset: it may be captured
+// into a HIP graph). Returns SV_OK, or SV_ERR_HIP when the fill could not be launched.
+__attribute__((visibility("hidden"))) int sv_internal_zero_fill(void* ws, size_t bytes,
+                                                                hipStream_t s);
+
 // Records that the library is about to leave untagged words in ws (per-position Markov launches,
 // top-K tables): the next call that takes tags on ws zero-fills it first.
 __attribute__((visibility("hidden"))) void sv_internal_untagged_use(void* ws);

@@ -1908,6 +1908,7 @@ int launch_greedy(const GreedyArgs& a, long groups, hipStream_t stream) {
 // the host it is only a stand-in for the symbol): the device address comes from
 // hipGetSymbolAddress, once per device with that device current, and is kept here.
 constexpr size_t kScratchBytes = (size_t)16 << 20;
+constexpr uint32_t kScratchTag = 1;  // the one tag of calls on the scratch (cleared before each)
 }  // namespace
 
 static __device__ __align__(256) uint64_t scratch[kScratchBytes / 8];
@@ -1961,13 +1962,17 @@ const char* sv_status_string(int status) {
 
 const char* sv_last_error(void) { return g_last_error.c_str(); }
 
-int sv_verify_batch(const void* target_logits, const void* draft_logits, int dtype, int B, int K,
-                    int V, float temperature, const int32_t* draft_tokens,
-                    const int32_t* num_draft, const float* uniforms,
-                    const float* residual_uniform, int32_t* accepted_len, int32_t* committed,
-                    float* target_prob, float* draft_prob, void* workspace,
-                    size_t workspace_bytes, void* stream) {
-  g_last_error.clear();
+}  // extern "C"
+
+namespace {
+
+// sv_verify_batch; with fixed_tag != 0 the call's tag is that value instead of one drawn from the
+// call counter (the caller has zero-filled the workspace words the call uses on `stream`).
+int verify_batch(const void* target_logits, const void* draft_logits, int dtype, int B, int K,
+                 int V, float temperature, const int32_t* draft_tokens, const int32_t* num_draft,
+                 const float* uniforms, const float* residual_uniform, int32_t* accepted_len,
+                 int32_t* committed, float* target_prob, float* draft_prob, void* workspace,
+                 size_t workspace_bytes, void* stream, uint32_t fixed_tag) {
   int st = check_shape(B, K, V);
   if (st != SV_OK) return st;
   if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16)
@@ -2008,8 +2013,12 @@ int sv_verify_batch(const void* target_logits, const void* draft_logits, int dty
   hipStream_t s = static_cast<hipStream_t>(stream);
   // a fresh call tag: words published by earlier calls (or the zeros of a fresh workspace)
   // never pass for this call's
-  st = sv_internal_call_tags(1, workspace, workspace_bytes, s, &a.tag);
-  if (st != SV_OK) return st;
+  if (fixed_tag != 0) {
+    a.tag = fixed_tag;
+  } else {
+    st = sv_internal_call_tags(1, workspace, workspace_bytes, s, &a.tag);
+    if (st != SV_OK) return st;
+  }
   a.stats = reinterpret_cast<uint64_t*>(ws + L.stats);
   a.gath = reinterpret_cast<uint64_t*>(ws + L.gath);
   a.ctot = reinterpret_cast<uint64_t*>(ws + L.ctot);
@@ -2028,6 +2037,22 @@ int sv_verify_batch(const void* target_logits, const void* draft_logits, int dty
                : launch_sample<float, false, false>(a, groups, s);
   return vec ? launch_sample<uint16_t, true, false>(a, groups, s)
              : launch_sample<uint16_t, false, false>(a, groups, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int sv_verify_batch(const void* target_logits, const void* draft_logits, int dtype, int B, int K,
+                    int V, float temperature, const int32_t* draft_tokens,
+                    const int32_t* num_draft, const float* uniforms,
+                    const float* residual_uniform, int32_t* accepted_len, int32_t* committed,
+                    float* target_prob, float* draft_prob, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  return verify_batch(target_logits, draft_logits, dtype, B, K, V, temperature, draft_tokens,
+                      num_draft, uniforms, residual_uniform, accepted_len, committed,
+                      target_prob, draft_prob, workspace, workspace_bytes, stream, 0u);
 }
 
 int sv_verify_batch_noalloc(const void* target_logits, const void* draft_logits, int dtype, int B,
@@ -2049,11 +2074,21 @@ int sv_verify_batch_noalloc(const void* target_logits, const void* draft_logits,
                                         " the library holds per GPU; call sv_verify_batch with a "
                                         "workspace instead");
   void* ws = nullptr;
-  const int st = scratch_of_current_device(&ws);
+  int st = scratch_of_current_device(&ws);
   if (st != SV_OK) return st;
-  return sv_verify_batch(target_logits, draft_logits, dtype, B, K, V, temperature, draft_tokens,
-                         num_draft, uniforms, residual_uniform, accepted_len, committed,
-                         target_prob, draft_prob, ws, need, stream);
+  // Every call clears the scratch words it uses and hands off under one fixed tag, so that the
+  // same launches are correct when a captured call is replayed: nothing depends on the host's
+  // call counter. Validation first, so that a rejected call enqueues nothing.
+  st = verify_batch(target_logits, draft_logits, dtype, B, K, V, temperature, draft_tokens,
+                    num_draft, uniforms, residual_uniform, accepted_len, committed, target_prob,
+                    draft_prob, nullptr, 0, stream, kScratchTag);
+  if (st != SV_ERR_WORKSPACE) return st == SV_OK ? fail(SV_ERR_HIP, "unreachable") : st;
+  g_last_error.clear();
+  st = sv_internal_zero_fill(ws, need, static_cast<hipStream_t>(stream));
+  if (st != SV_OK) return st;
+  return verify_batch(target_logits, draft_logits, dtype, B, K, V, temperature, draft_tokens,
+                      num_draft, uniforms, residual_uniform, accepted_len, committed, target_prob,
+                      draft_prob, ws, need, stream, kScratchTag);
 }
 
 int sv_verify_ragged(const void* target_logits, const void* draft_logits, int dtype, int B,

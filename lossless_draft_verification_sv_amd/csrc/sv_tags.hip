@@ -73,6 +73,10 @@ int sv_internal_call_tags(uint32_t step, void* ws, size_t bytes, hipStream_t s, 
   return need ? fill(ws, from, bytes, s) : SV_OK;
 }
 
+int sv_internal_zero_fill(void* ws, size_t bytes, hipStream_t s) {
+  return fill(ws, 0, bytes & ~(size_t)7, s);
+}
+
 void sv_internal_untagged_use(void* ws) {
   std::lock_guard<std::mutex> lock(g_mu);
   g_seen.erase(reinterpret_cast<uintptr_t>(ws));
