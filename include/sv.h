@@ -41,7 +41,10 @@
  *    number that is handed out again. Memory that held other data since the library last used
  *    it as a workspace must be zeroed by the caller (hipMemset or torch.zeros) before it is
  *    passed again. One workspace must not be used by two calls that can run at the same time
- *    (e.g. on two streams).
+ *    (e.g. on two streams). The stamp is fixed when the call is enqueued, so a call captured
+ *    into a HIP graph must not be replayed: a replay would take the words of the one before
+ *    for its own. sv_verify_batch_noalloc is the entry point whose captured calls replay
+ *    correctly.
  *  - A work-group waiting for partials from other work-groups of the same call gives up after a
  *    bounded time (about two seconds) and then stores -2 in that request's accepted_len. This
  *    does not happen in normal operation.
