@@ -528,6 +528,30 @@ def test_masking_k0_out_of_range_and_residual_support():
     check_masking_and_edges()
 
 
+def test_tokens_without_mass_under_one_distribution():
+    """The accept rule min(1, p/q) at its limits (a -inf logit is probability 0): a token the
+    draft gives no mass (q = 0) is kept whenever the target gives it mass, for any u in [0, 1);
+    a token the target gives no mass (p = 0) is always rejected, its target probability is 0,
+    and the residual draw then follows max(0, p - q) without it."""
+    T = np.array([[0.5, -1.0, 2.0, 0.0], [0.0, 0.0, 0.0, 0.0]], np.float32)
+    D = np.array([[-np.inf, 0.3, 1.0, 0.2]], np.float32)
+    for u in (0.0, 0.5, 0.999999):
+        res = call(T, D, [0], [u], 0.5, 1.0)
+        assert res.n == 1 and res.committed[0] == 0
+        assert res.draft_prob[0] == 0.0 and res.target_prob[0] > 0.0
+    T2 = T.copy()
+    T2[0, 1] = -np.inf
+    p = scipy_probs(T2[0], 1.0)
+    q = scipy_probs(D[0], 1.0)
+    w = np.maximum(0.0, p - q)
+    assert w[1] == 0.0
+    for u in (0.0, 0.5):
+        for v, lo, hi in residual_intervals(w):
+            res = call(T2, D, [1], [u], (lo + hi) / 2, 1.0)
+            assert res.n == 0 and res.committed == [v, -1] and v != 1
+            assert res.target_prob[0] == 0.0 and res.draft_prob[0] > 0.0
+
+
 def test_batch_driver_matches_per_request():
     from workloads import TINY, generate
 

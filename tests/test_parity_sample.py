@@ -154,6 +154,28 @@ def test_masked_vocabulary(V, dtype):
     assert np.all(acc[0::2] == K)  # identical masked rows: every draft kept
 
 
+@pytest.mark.parametrize("V,dtype", [(4096, "f32"), (4096, "bf16"), (4099, "f32")])
+def test_tokens_without_mass_under_one_distribution(V, dtype):
+    """Slot 0's token has a -inf draft logit (q = 0) and a finite target logit: kept for any
+    uniform; slot 1's token has a -inf target logit (p = 0): rejected, with target probability
+    0 and the residual draw avoiding it. Probabilities are 0, never NaN."""
+    inp = generate(TINY.replace(name=f"zero_mass_V{V}_{dtype}", B=4, K=3, V=V, dtype=dtype,
+                                seed=91 + V % 5))
+    neg_inf = np.uint16(0xFF80) if dtype == "bf16" else np.float32(-np.inf)
+    for b in range(4):
+        inp.draft[b, 0, inp.tokens[b, 0]] = neg_inf
+        inp.target[b, 1, inp.tokens[b, 1]] = neg_inf
+    inp.uniforms[:, 0] = np.array([0.0, 0.5, 0.9, 0.999], np.float32)
+    inp.uniforms[:, 1] = 0.3
+    s = _check(inp)
+    assert s["ambiguous"] == 0
+    acc, com, tp, dp = run_sample(inp.target, inp.draft, inp.tokens, inp.uniforms, inp.residual,
+                                  inp.workload.temperature)
+    assert np.all(acc == 1) and np.all(dp[:, 0] == 0.0) and np.all(tp[:, 0] > 0.0)
+    assert np.all(tp[:, 1] == 0.0) and np.all(com[:, 1] != inp.tokens[:, 1])
+    assert not np.isnan(tp).any() and not np.isnan(dp).any()
+
+
 @pytest.mark.parametrize("tau", [0.05, 20.0])
 def test_extreme_temperatures(tau):
     w = TINY.replace(name=f"temperature_{tau}", B=6, K=4, V=8000, dtype="bf16",
