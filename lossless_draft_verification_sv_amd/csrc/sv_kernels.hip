@@ -42,6 +42,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <climits>
 #include <cstdio>
 #include <mutex>
@@ -1855,11 +1856,13 @@ int segments_per_row(int V, int dtype, bool vec, const Plan& p) {
   return ns <= p.NSmax ? (int)ns : 0;
 }
 
-// Work-groups of `kernel` resident at once on the current device (cached per device).
-long resident_groups(const void* kernel, long* cache) {
+// Work-groups of `kernel` resident at once on the current device (cached per device; host
+// threads that fill an entry at the same time store the same value).
+long resident_groups(const void* kernel, std::atomic<long>* cache) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 1536;
-  if (cache[dev] == 0) {
+  long n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0) != hipSuccess ||
         per_cu < 1)
@@ -1867,16 +1870,17 @@ long resident_groups(const void* kernel, long* cache) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus < 1)
       cus = 256;
-    cache[dev] = (long)per_cu * cus;
+    n = (long)per_cu * cus;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 template <typename T, bool VEC, bool GEN>
 int launch_sample(const SampleArgs& args, long groups, hipStream_t stream) {
   const void* kernel = GEN ? reinterpret_cast<const void*>(&sv_verify_ragged_kernel<T, VEC>)
                            : reinterpret_cast<const void*>(&sv_verify_sample<T, VEC>);
-  static long cache[kMaxDevices] = {};
+  static std::atomic<long> cache[kMaxDevices] = {};
   SampleArgs a = args;
   // The lag: about the number of requests whose row-stat groups are resident at once, plus two.
   // In ragged batches (verify lengths per request) the rows past k_b are skipped, so the host

@@ -17,11 +17,12 @@
 
 #include <hip/hip_runtime.h>
 
-
 #include <float.h>
 #include <limits.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <atomic>
 
 #include "sv.h"
 #include "sv_internal.h"
@@ -1533,19 +1534,20 @@ __global__ __launch_bounds__(kThreads) void markov_finish_sampled(
 
 bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; host threads that fill an entry at
+// the same time store the same value).
 int cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 // The argmax head takes the pipelined kernel (markov_pipe), the sampled head markov_resident.
