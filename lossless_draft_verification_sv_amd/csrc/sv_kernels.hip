@@ -72,6 +72,7 @@ constexpr int kSpinLimit = 1 << 21;  // polls (about 1 us each) before a waiting
 constexpr int32_t kTimedOut = -2;    // accepted_len value reported by a group that gave up
 constexpr int kPollSleep = 2;        // s_sleep units (64 clocks each) between two polls
 constexpr int kMaxDevices = 64;      // devices the host-side caches keep an entry for
+constexpr int kBf16Chunks = 6;       // chunks per bf16 row, at most
 
 // ---------------------------------------------------------------------------------------------
 // Work decomposition (host side, shared by the workspace query and the launches).
@@ -1878,11 +1879,17 @@ long resident_groups(const void* kernel, std::atomic<long>* cache) {
 }
 
 template <typename T, bool VEC, bool GEN>
-int launch_sample(const SampleArgs& args, long groups, hipStream_t stream) {
+int launch_sample(const SampleArgs& args, hipStream_t stream) {
   const void* kernel = GEN ? reinterpret_cast<const void*>(&sv_verify_ragged_kernel<T, VEC>)
                            : reinterpret_cast<const void*>(&sv_verify_sample<T, VEC>);
   static std::atomic<long> cache[kMaxDevices] = {};
   SampleArgs a = args;
+  // 16-byte bf16 rows: at most kBf16Chunks chunks per row (chunks of about three rounds of 16-byte loads
+  // at V = 151936). The plan sizes the workspace for the plan's C; fewer chunks use less of it.
+  // Measured at V = 151936, K = 8: 11.6-25 us against 12-40 us for the plan's 12-37 chunks at
+  // B = 1-32 (its 6 at B = 64); float32 rows keep the plan's count (B = 1: 37 chunks measured
+  // best, one round each).
+  if (VEC && sizeof(T) == 2 && a.C > kBf16Chunks) a.C = kBf16Chunks;
   // The lag: about the number of requests whose row-stat groups are resident at once, plus two.
   // In ragged batches (verify lengths per request) the rows past k_b are skipped, so the host
   // cannot tell how many requests stream at once; a lag too short makes draw groups wait for
@@ -1892,6 +1899,8 @@ int launch_sample(const SampleArgs& args, long groups, hipStream_t stream) {
   long L = (resident_groups(kernel, cache) + per_request - 1) / per_request + 2;
   if (GEN || a.num_draft != nullptr || L > a.B) L = a.B;
   a.L = (int)L;
+  // the grid of this C: the row-stat groups, then the draw groups
+  const long groups = (long)a.B * (2L * a.K + 1) * a.C + (long)a.B * a.C2;
   if (GEN)
     hipLaunchKernelGGL((sv_verify_ragged_kernel<T, VEC>), dim3((unsigned)groups), dim3(kBlock),
                        0, stream, a);
@@ -2038,10 +2047,10 @@ int verify_batch(const void* target_logits, const void* draft_logits, int dtype,
   a.temps = nullptr;
   a.NS = segments_per_row(V, dtype, vec, p);
   if (dtype == SV_DTYPE_F32)
-    return vec ? launch_sample<float, true, false>(a, groups, s)
-               : launch_sample<float, false, false>(a, groups, s);
-  return vec ? launch_sample<uint16_t, true, false>(a, groups, s)
-             : launch_sample<uint16_t, false, false>(a, groups, s);
+    return vec ? launch_sample<float, true, false>(a, s)
+               : launch_sample<float, false, false>(a, s);
+  return vec ? launch_sample<uint16_t, true, false>(a, s)
+             : launch_sample<uint16_t, false, false>(a, s);
 }
 
 }  // namespace
@@ -2164,10 +2173,10 @@ int sv_verify_ragged(const void* target_logits, const void* draft_logits, int dt
   const bool vec = rows_vectorisable(target_logits, a.draft, dtype, V);
   a.NS = segments_per_row(V, dtype, vec, p);
   if (dtype == SV_DTYPE_F32)
-    return vec ? launch_sample<float, true, true>(a, groups, s)
-               : launch_sample<float, false, true>(a, groups, s);
-  return vec ? launch_sample<uint16_t, true, true>(a, groups, s)
-             : launch_sample<uint16_t, false, true>(a, groups, s);
+    return vec ? launch_sample<float, true, true>(a, s)
+               : launch_sample<float, false, true>(a, s);
+  return vec ? launch_sample<uint16_t, true, true>(a, s)
+             : launch_sample<uint16_t, false, true>(a, s);
 }
 
 int sv_verify_greedy(const void* target_logits, int dtype, int B, int K, int V,
