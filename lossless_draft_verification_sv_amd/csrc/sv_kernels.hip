@@ -72,7 +72,8 @@ constexpr int kSpinLimit = 1 << 21;  // polls (about 1 us each) before a waiting
 constexpr int32_t kTimedOut = -2;    // accepted_len value reported by a group that gave up
 constexpr int kPollSleep = 2;        // s_sleep units (64 clocks each) between two polls
 constexpr int kMaxDevices = 64;      // devices the host-side caches keep an entry for
-constexpr int kBf16Chunks = 6;       // chunks per bf16 row, at most
+constexpr int kBf16Chunks = 6;       // chunks per 16-byte bf16 row, at most
+constexpr int kF32Chunks = 12;       // chunks per 16-byte float32 row, at most (larger batches)
 
 // ---------------------------------------------------------------------------------------------
 // Work decomposition (host side, shared by the workspace query and the launches).
@@ -1884,12 +1885,15 @@ int launch_sample(const SampleArgs& args, hipStream_t stream) {
                            : reinterpret_cast<const void*>(&sv_verify_sample<T, VEC>);
   static std::atomic<long> cache[kMaxDevices] = {};
   SampleArgs a = args;
-  // 16-byte bf16 rows: at most kBf16Chunks chunks per row (chunks of about three rounds of 16-byte loads
-  // at V = 151936). The plan sizes the workspace for the plan's C; fewer chunks use less of it.
-  // Measured at V = 151936, K = 8: 11.6-25 us against 12-40 us for the plan's 12-37 chunks at
-  // B = 1-32 (its 6 at B = 64); float32 rows keep the plan's count (B = 1: 37 chunks measured
-  // best, one round each).
+  // Fewer, longer chunks than the plan's for 16-byte rows (the plan sizes the workspace for its
+  // C; fewer chunks use less of it): at most kBf16Chunks per bf16 row, and kF32Chunks per float32
+  // row once that still leaves 1024 row-stat groups (about three rounds of 16-byte loads per
+  // chunk at V = 151936; fewer partials for the decision to gather). Measured at V = 151936,
+  // K = 8 against the plan's 12-37 chunks: bf16 B = 1-48 3-30% faster, float32 B = 8-16 10-17%
+  // faster, B = 1-4 the same or slower with 12 (there 37 chunks of one round each fill the GPU).
   if (VEC && sizeof(T) == 2 && a.C > kBf16Chunks) a.C = kBf16Chunks;
+  if (VEC && sizeof(T) == 4 && a.C > kF32Chunks && (long)a.B * (2 * a.K + 1) * kF32Chunks >= 1024)
+    a.C = kF32Chunks;
   // The lag: about the number of requests whose row-stat groups are resident at once, plus two.
   // In ragged batches (verify lengths per request) the rows past k_b are skipped, so the host
   // cannot tell how many requests stream at once; a lag too short makes draw groups wait for
