@@ -725,18 +725,53 @@ __device__ __forceinline__ void res_tile(const ResArgs& a, T* __restrict__ out,
   lds_barrier();  // sz is rewritten by the next tile
 }
 
+// Cross-lane moves inside the vector ALU (DPP), for the reductions and scans of the draws: each
+// lane combines the lanes 1, 2, 4 and 8 below it inside its row of 16, then lane 15 of rows 0
+// and 2 is folded into rows 1 and 3 and lane 31 into rows 2 and 3, so lane l ends up with the
+// combination of lanes 0..l (lane 63: the whole wave). A source lane outside the row, or a row
+// that the mask leaves out, reads the identity. Every call runs with the whole wave active.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t x, uint32_t identity) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)x, CTRL, ROWS, 0xf, false);
+}
+#define SV_MK_SCAN(STEP) \
+  STEP(0x111, 0xf);      \
+  STEP(0x112, 0xf);      \
+  STEP(0x114, 0xf);      \
+  STEP(0x118, 0xf);      \
+  STEP(0x142, 0xa);      \
+  STEP(0x143, 0xc)
+
+// Inclusive prefix sum over the wave (fp32), and the exclusive one (the inclusive sum of the lane
+// below, by a whole-wave shift; lane 0: 0).
+__device__ __forceinline__ float wave_incl_sum(float x) {
+#define SV_STEP(C, R) x += __uint_as_float(dpp_move<C, R>(__float_as_uint(x), 0u))
+  SV_MK_SCAN(SV_STEP);
+#undef SV_STEP
+  return x;
+}
+__device__ __forceinline__ float wave_excl_of(float incl) {
+  return __uint_as_float(dpp_move<0x138, 0xf>(__float_as_uint(incl), 0u));  // wave_shr:1
+}
+__device__ __forceinline__ float wave_max_all(float x) {  // NaN-free inputs
+#define SV_STEP(C, R) x = fmaxf(x, __uint_as_float(dpp_move<C, R>(__float_as_uint(x), 0xff800000u)))
+  SV_MK_SCAN(SV_STEP);
+#undef SV_STEP
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(x), 63));
+}
+__device__ __forceinline__ int wave_min_all(int x) {
+#define SV_STEP(C, R) x = min(x, (int)dpp_move<C, R>((uint32_t)x, (uint32_t)INT_MAX))
+  SV_MK_SCAN(SV_STEP);
+#undef SV_STEP
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
 // Sum over the work-group of one value per thread: returns this thread's exclusive prefix (in
 // thread order) and the total through `total`. s_w: kWaves floats of LDS. Every thread calls it.
 __device__ __forceinline__ float block_scan_excl(float x, float* s_w, float& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float incl = x;
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) {
-    const float t = __shfl_up(incl, s);
-    incl = lane >= s ? incl + t : incl;
-  }
-  float excl = __shfl_up(incl, 1);
-  excl = lane == 0 ? 0.0f : excl;
+  const float incl = wave_incl_sum(x);
+  const float excl = wave_excl_of(incl);
   if (lane == 63) s_w[wave] = incl;
   lds_barrier();
   float before = 0.0f, all = 0.0f;
@@ -751,8 +786,7 @@ __device__ __forceinline__ float block_scan_excl(float x, float* s_w, float& tot
 }
 
 __device__ __forceinline__ float block_max(float x, float* s_w) {
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) x = fmaxf(x, __shfl_xor(x, s));
+  x = wave_max_all(x);
   if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = x;
   lds_barrier();
   float r = s_w[0];
@@ -763,8 +797,7 @@ __device__ __forceinline__ float block_max(float x, float* s_w) {
 }
 
 __device__ __forceinline__ int block_min_i(int x, int* s_w) {
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) x = min(x, __shfl_xor(x, s));
+  x = wave_min_all(x);
   if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = x;
   lds_barrier();
   int r = s_w[0];
@@ -783,8 +816,8 @@ __device__ __forceinline__ int block_min_i(int x, int* s_w) {
 // infinite target. Without mass the token is 0, after a wait that gave up kResFailed: then the
 // token itself is published, with kNoOwner as the decision.
 __device__ __forceinline__ void res_decide(const ResArgs& a, int b, int k, uint32_t tg, float c,
-                                           bool failed, float* s_f, int* s_i, float* s_tgt1,
-                                           float* s_pm, float* s_ps) {
+                                           bool failed, float* s_f, int* s_i, int* s_i2,
+                                           float* s_tgt1, float* s_pm, float* s_ps) {
   const int tid = threadIdx.x;
   const uint64_t* row = a.part + (size_t)b * a.nwg * 2;
   // the partials into LDS, one per thread at a time
@@ -840,11 +873,33 @@ __device__ __forceinline__ void res_decide(const ResArgs& a, int b, int k, uint3
     }
     P += x;
   }
-  const int jf = block_min_i(found, s_i);
-  if (found == jf && jf != INT_MAX) *s_tgt1 = tgt;
-  const int jl = -block_min_i(-last, s_i);
+  // one exchange for the first work-group past the target (with its target, from the lane that
+  // found it: partial indices are distinct) and the last one with mass
+  {
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wf = wave_min_all(found);
+    const uint64_t who = __ballot(found == wf && wf != INT_MAX);
+    const float wt =
+        who != 0 ? __uint_as_float((uint32_t)__builtin_amdgcn_readlane(
+                       (int)__float_as_uint(tgt), (int)__ffsll((long long)who) - 1))
+                 : 0.0f;
+    const int wl = -wave_min_all(-last);
+    if (lane == 0) {
+      s_i[wave] = wf;
+      s_f[wave] = wt;
+      s_i2[wave] = wl;
+    }
+  }
   lds_barrier();
   if (tid == 0) {
+    int jf = INT_MAX, jl = -1;
+    for (int v = 0; v < kWaves; ++v) {
+      if (s_i[v] < jf) {
+        jf = s_i[v];
+        *s_tgt1 = s_f[v];
+      }
+      jl = max(jl, s_i2[v]);
+    }
     int token = -1;
     if (failed || any_late) token = kResFailed;
     else if (!(S > 0.0f) || jl < 0) token = 0;
@@ -876,19 +931,21 @@ __device__ __forceinline__ void res_owner_draw(const ResArgs& a, const T* __rest
   const int E = (n + 63) >> 6;  // <= kResItems
   const T* row = out + ((size_t)b * a.K + k) * (size_t)a.V + v0 + lane * E;
   const int mine = n - lane * E < E ? n - lane * E : E;  // this lane's entries (may be <= 0)
-  float lsum = 0.0f;
-  for (int i = 0; i < mine; ++i) lsum += draw_weight(Logit<T>::get(row[i]), m, c);
-  float incl = lsum;
+  // the lane's entries, all loads in flight together, weighed once and kept for the walk
+  float wv[kResItems];
 #pragma unroll
-  for (int s = 1; s < 64; s <<= 1) {
-    const float t = __shfl_up(incl, s);
-    incl = lane >= s ? incl + t : incl;
-  }
-  float cum = __shfl_up(incl, 1);
-  cum = lane == 0 ? 0.0f : cum;
+  for (int i = 0; i < kResItems; ++i)
+    wv[i] = i < mine ? draw_weight(Logit<T>::get(row[i]), m, c) : 0.0f;
+  float lsum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kResItems; ++i)
+    if (i < mine) lsum += wv[i];
+  const float incl = wave_incl_sum(lsum);
+  float cum = wave_excl_of(incl);
   int pick = -1, lastw = -1;
-  for (int i = 0; i < mine; ++i) {  // the same weights again (the entries are in the cache)
-    const float w = draw_weight(Logit<T>::get(row[i]), m, c);
+#pragma unroll
+  for (int i = 0; i < kResItems; ++i) {  // the same weights in the same order
+    const float w = i < mine ? wv[i] : 0.0f;
     if (w > 0.0f) {
       cum += w;
       pick = (pick < 0 && cum > target) ? i : pick;
@@ -999,7 +1056,7 @@ markov_resident(const T* __restrict__ base, T* __restrict__ out, ResArgs a) {
     // 4. work-group b < B: the token of request b (or, drawing, who draws it)
     const int mode = (SAMPLED && w < a.B) ? s_mode[w] : 0;
     if (w < a.B && mode == 1) {
-      res_decide(a, w, k, tg, s_c[w], s_tok[w] == kResFailed, s_best, s_bi, s_tgt1, s_pm,
+      res_decide(a, w, k, tg, s_c[w], s_tok[w] == kResFailed, s_best, s_bi, s_late, s_tgt1, s_pm,
                  s_ps);
     } else if (w < a.B && mode == 2) {
       if (tid == 0) {
@@ -1099,8 +1156,15 @@ markov_resident(const T* __restrict__ base, T* __restrict__ out, ResArgs a) {
         s_tgt[tid] = t;
       }
       __syncthreads();  // also: this work-group's stores of the corrected rows are complete
-      for (int b = wave; b < a.B; b += kWaves)
-        if (s_own[b]) res_owner_draw<T>(a, out, b, k, tg, t0, nit, s_m[b], s_c[b], s_tgt[b]);
+      // the i-th draw this work-group owns goes to wave i mod 4: a work-group that owns several
+      // spreads them over its waves
+      const uint64_t owned = __ballot(lane < a.B && s_own[lane] != 0);  // the same in every wave
+      int i = 0;
+      for (uint64_t m = owned; m != 0; m &= m - 1, ++i) {
+        if (i % kWaves != wave) continue;
+        const int b = __ffsll((long long)m) - 1;
+        res_owner_draw<T>(a, out, b, k, tg, t0, nit, s_m[b], s_c[b], s_tgt[b]);
+      }
     }
     lds_barrier();  // s_tok, s_best are rewritten at the next position
   }
