@@ -80,6 +80,47 @@ __device__ __forceinline__ bool better(float z, int i, float best, int bi) {
   return z > best || (z == best && i < bi);
 }
 
+// Exchanges inside the vector ALU (DPP, every lane of the wave active): the value of lane l ^ 1
+// and of lane l ^ 2 (quad permutes), and of the mirror lane inside each group of 8 and of 16.
+// After the quad steps every quad holds one value, so the mirror in 8 brings the other quad's;
+// after that the mirror in 16 brings the other group of 8's.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+template <int CTRL>
+__device__ __forceinline__ float dpp_xchg_f32(float x) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)__float_as_uint(x), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& best, int& bi) {
+  const float b2 = dpp_xchg_f32<CTRL>(best);
+  const int i2 = __builtin_amdgcn_mov_dpp(bi, CTRL, 0xf, 0xf, false);
+  if (better(b2, i2, best, bi)) {
+    best = b2;
+    bi = i2;
+  }
+}
+// The wave's argmax, (largest value, lowest index among equals), in every lane: within rows of
+// 16 on DPP, then the four rows' results (lanes 0, 16, 32, 48) read out and combined.
+__device__ __forceinline__ void wave_argmax(float& best, int& bi) {
+  argmax_step<kDppXor1>(best, bi);
+  argmax_step<kDppXor2>(best, bi);
+  argmax_step<kDppHalfMirror>(best, bi);
+  argmax_step<kDppMirror>(best, bi);
+  float rb = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(best), 0));
+  int ri = __builtin_amdgcn_readlane(bi, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const float b2 =
+        __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(best), 16 * r));
+    const int i2 = __builtin_amdgcn_readlane(bi, 16 * r);
+    if (better(b2, i2, rb, ri)) {
+      rb = b2;
+      ri = i2;
+    }
+  }
+  best = rb;
+  bi = ri;
+}
+
 // Work-group g of a position covers vocabulary tile g / nrb and request block g % nrb; the
 // launch index is spread so that the work-groups of one XCD (launch index mod 8) take a
 // contiguous range of g, and so the request blocks of a tile share that XCD's L2.
@@ -183,15 +224,8 @@ __global__ __launch_bounds__(kThreads) void markov_bias_tile(
       bi = tile * kTileV + col;
     }
   }
-#pragma unroll
-  for (int s = 1; s <= 2; s <<= 1) {
-    const float b2 = __shfl_xor(best, s);
-    const int i2 = __shfl_xor(bi, s);
-    if (better(b2, i2, best, bi)) {
-      best = b2;
-      bi = i2;
-    }
-  }
+argmax_step<kDppXor1>(best, bi);
+argmax_step<kDppXor2>(best, bi);
   const int b = b0 + m;
   if (q == 0 && b < B)
     part[(size_t)b * ntile + tile] = ((uint64_t)__float_as_uint(best) << 32) | (uint32_t)bi;
@@ -429,15 +463,8 @@ __device__ __forceinline__ void stream_item(const StreamArgs& a, const T* __rest
           if (e < ncol) Logit<T>::put(orow + e, z[e]);
       }
     }
-#pragma unroll
-    for (int s = 1; s <= 2; s <<= 1) {
-      const float b2 = __shfl_xor(best, s);
-      const int i2 = __shfl_xor(bi, s);
-      if (better(b2, i2, best, bi)) {
-        best = b2;
-        bi = i2;
-      }
-    }
+argmax_step<kDppXor1>(best, bi);
+argmax_step<kDppXor2>(best, bi);
   }
   if (q == 0 && b < a.B)
     a.part[(size_t)b * a.ntile + tile] = ((uint64_t)__float_as_uint(best) << 32) | (uint32_t)bi;
@@ -505,14 +532,7 @@ __global__ __launch_bounds__(kThreads) void markov_finish(const uint64_t* __rest
       }
     }
   }
-  for (int s = 32; s >= 1; s >>= 1) {
-    const float b2 = __shfl_xor(best, s);
-    const int i2 = __shfl_xor(bi, s);
-    if (better(b2, i2, best, bi)) {
-      best = b2;
-      bi = i2;
-    }
-  }
+  wave_argmax(best, bi);
   __shared__ float sb[kWaves];
   __shared__ int si[kWaves];
   if ((threadIdx.x & 63) == 0) {
@@ -686,15 +706,8 @@ __device__ __forceinline__ void res_tile(const ResArgs& a, T* __restrict__ out,
           if (e < ncol) Logit<T>::put(orow + e, z[e]);
       }
     }
-#pragma unroll
-    for (int sh = 1; sh <= 2; sh <<= 1) {
-      const float b2 = __shfl_xor(best, sh);
-      const int i2 = __shfl_xor(bi, sh);
-      if (better(b2, i2, best, bi)) {
-        best = b2;
-        bi = i2;
-      }
-    }
+argmax_step<kDppXor1>(best, bi);
+argmax_step<kDppXor2>(best, bi);
     if (better(best, bi, run, run_i)) {
       run = best;
       run_i = bi;
@@ -710,14 +723,14 @@ __device__ __forceinline__ void res_tile(const ResArgs& a, T* __restrict__ out,
         y[e] = (row_ok && e < ncol) ? y[e] : -INFINITY;
         tm = y[e] > tm ? y[e] : tm;
       }
-      tm = fmaxf(tm, __shfl_xor(tm, 1));
-      tm = fmaxf(tm, __shfl_xor(tm, 2));
+      tm = fmaxf(tm, dpp_xchg_f32<kDppXor1>(tm));
+      tm = fmaxf(tm, dpp_xchg_f32<kDppXor2>(tm));
       const float nm = fmaxf(sm, tm);
       float ts = 0.0f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) ts += draw_weight(y[e], nm, c);
-      ts += __shfl_xor(ts, 1);
-      ts += __shfl_xor(ts, 2);
+      ts += dpp_xchg_f32<kDppXor1>(ts);
+      ts += dpp_xchg_f32<kDppXor2>(ts);
       ss = ss * (sm == nm ? 1.0f : __builtin_amdgcn_exp2f((sm - nm) * c)) + ts;
       sm = nm;
     }
@@ -958,10 +971,10 @@ __device__ __forceinline__ void res_owner_draw(const ResArgs& a, const T* __rest
   int L, e;
   if (hit != 0) {
     L = __builtin_ctzll(hit);
-    e = __shfl(pick, L);
+    e = __builtin_amdgcn_readlane(pick, L);
   } else if (mass != 0) {
     L = 63 - __builtin_clzll(mass);
-    e = __shfl(lastw, L);
+    e = __builtin_amdgcn_readlane(lastw, L);
   } else {
     L = 0;
     e = 0;
@@ -1106,15 +1119,7 @@ markov_resident(const T* __restrict__ base, T* __restrict__ out, ResArgs a) {
           }
         }
       }
-#pragma unroll
-      for (int sh = 32; sh >= 1; sh >>= 1) {
-        const float b2 = __shfl_xor(best, sh);
-        const int i2 = __shfl_xor(bi, sh);
-        if (better(b2, i2, best, bi)) {
-          best = b2;
-          bi = i2;
-        }
-      }
+wave_argmax(best, bi);
       const bool wave_late = __ballot(late) != 0;
       if (lane == 0) {
         s_best[wave] = best;
@@ -1327,15 +1332,9 @@ __device__ __forceinline__ void pipe_tile(const ResArgs& a, T* __restrict__ out,
           if (e < ncol) Logit<T>::put(orow + e, z[e]);
       }
     }
-#pragma unroll
-    for (int sh = 1; sh <= 4; sh <<= 1) {
-      const float b2 = __shfl_xor(best, sh);
-      const int i2 = __shfl_xor(bi, sh);
-      if (better(b2, i2, best, bi)) {
-        best = b2;
-        bi = i2;
-      }
-    }
+argmax_step<kDppXor1>(best, bi);
+argmax_step<kDppXor2>(best, bi);
+argmax_step<kDppHalfMirror>(best, bi);
     if (better(best, bi, run, run_i)) {
       run = best;
       run_i = bi;
@@ -1450,15 +1449,7 @@ markov_pipe(const T* __restrict__ base, T* __restrict__ out, ResArgs a) {
           }
         }
       }
-#pragma unroll
-      for (int sh = 32; sh >= 1; sh >>= 1) {
-        const float b2 = __shfl_xor(best, sh);
-        const int i2 = __shfl_xor(bi, sh);
-        if (better(b2, i2, best, bi)) {
-          best = b2;
-          bi = i2;
-        }
-      }
+wave_argmax(best, bi);
       const bool wave_late = __ballot(late) != 0;
       if (lane == 0) {
         s_best[wave] = best;
@@ -1539,14 +1530,7 @@ __global__ __launch_bounds__(kThreads) void markov_finish_sampled(
       }
     }
   }
-  for (int sh = 32; sh >= 1; sh >>= 1) {
-    const float b2 = __shfl_xor(best, sh);
-    const int i2 = __shfl_xor(bi, sh);
-    if (better(b2, i2, best, bi)) {
-      best = b2;
-      bi = i2;
-    }
-  }
+  wave_argmax(best, bi);
   if (lane == 0) {
     s_best[wave] = best;
     s_bi[wave] = bi;
