@@ -93,6 +93,24 @@ __device__ __forceinline__ float wave_max(float x) {
   return __int_as_float(__builtin_amdgcn_readlane(v, 63));
 }
 
+// (value, slot) order of a candidate pick: the larger value, then the lower slot.
+__device__ __forceinline__ bool pick_better(float z, int i, float best, int bi) {
+  return z > best || (z == best && i < bi);
+}
+// One exchange step of a pick over lanes, inside the vector ALU (DPP, every lane active): CTRL
+// 0xB1 and 0x4E swap lanes l ^ 1 and l ^ 2 inside each quad, 0x141 and 0x140 mirror each group
+// of 8 and of 16 lanes (after the steps before it each half of the group is uniform).
+template <int CTRL>
+__device__ __forceinline__ void pick_step(float& best, int& bi) {
+  const float b2 =
+      __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)__float_as_uint(best), CTRL, 0xf, 0xf, false));
+  const int i2 = __builtin_amdgcn_mov_dpp(bi, CTRL, 0xf, 0xf, false);
+  if (pick_better(b2, i2, best, bi)) {
+    best = b2;
+    bi = i2;
+  }
+}
+
 // Smallest and largest value over the wave's lanes (every lane gets them).
 __device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
 #define TOPK_UMAX1(C, R) v = max(v, (uint32_t)dpp_i32<C, R>((int)v, 0))
@@ -518,7 +536,7 @@ __global__ __launch_bounds__(kThreads) void topk_bias(
     int V, int kc, int low,
     const uint16_t* __restrict__ left, const uint16_t* __restrict__ right, int R,
     const int32_t* __restrict__ anchor, int32_t* __restrict__ cand, float* __restrict__ cand_val,
-    int32_t* __restrict__ cand_out, float* __restrict__ table) {
+    int32_t* __restrict__ cand_out, float* __restrict__ table, int32_t* __restrict__ next) {
   // the merge lists and the staged factor rows are used one after the other
   __shared__ union __attribute__((aligned(16))) {
     SelShared<kMergeList> m[2];
@@ -528,6 +546,9 @@ __global__ __launch_bounds__(kThreads) void topk_bias(
     } f;
   } lds;
   __shared__ int32_t cidx[2][kMaxCand];  // candidates of rows k-1 and k, -1 past kc
+  __shared__ float cval[kMaxCand];        // logits of row k's candidates
+  __shared__ float s_pv[kMaxCand][4];      // per table row, the pick over each 16 columns
+  __shared__ int s_pj[kMaxCand][4];
   uint16_t (*sa)[kRow] = lds.f.a;
   uint16_t (*sb)[kRow] = lds.f.b;
   const int r = blockIdx.x, b = r / K, k = r % K;
@@ -542,6 +563,7 @@ __global__ __launch_bounds__(kThreads) void topk_bias(
         cidx[1][slot] = v;
         cand[(size_t)r * kMaxCand + slot] = v;
         cand_val[(size_t)r * kMaxCand + slot] = key_value(key_of(e));
+        cval[slot] = key_value(key_of(e));
         if (cand_out != nullptr) cand_out[(size_t)r * kc + slot] = v;
       });
   // stage: thread covers rows tid / 32 + 8 u, word tid % 32; every load in flight first
@@ -581,69 +603,91 @@ __global__ __launch_bounds__(kThreads) void topk_bias(
 #pragma unroll
   for (int i = 0; i < 16; ++i)
     dst[(size_t)(i0 + 8 * (i / 4) + 4 * h + (i % 4)) * kMaxCand + j0 + c] = acc[i];
+  // The walk's choice after every previous slot: for table row i, the slot j < kc with the
+  // largest logit_j + M[i][j] (NaN never wins; among equals the lowest slot, the lowest
+  // vocabulary index), as the walk takes it after a previous token in slot i. Each row of 16
+  // lanes picks over its 16 columns on DPP; the four picks of a table row meet in LDS.
+  {
+    const int j = j0 + c;
+    const float cv = j < kc ? cval[j] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float z = cv + acc[i];
+      float pv = (j < kc && z == z) ? z : -INFINITY;
+      int pj = j;
+      pick_step<0xB1>(pv, pj);
+      pick_step<0x4E>(pv, pj);
+      pick_step<0x141>(pv, pj);
+      pick_step<0x140>(pv, pj);
+      if ((c & 15) == 15) {
+        const int row = i0 + 8 * (i / 4) + 4 * h + (i % 4);
+        s_pv[row][2 * (wave & 1) + (c >> 4)] = pv;
+        s_pj[row][2 * (wave & 1) + (c >> 4)] = pj;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < kMaxCand) {
+    float pv = s_pv[tid][0];
+    int pj = s_pj[tid][0];
+#pragma unroll
+    for (int q = 1; q < 4; ++q)
+      if (pick_better(s_pv[tid][q], s_pj[tid][q], pv, pj)) {
+        pv = s_pv[tid][q];
+        pj = s_pj[tid][q];
+      }
+    next[(size_t)r * kMaxCand + tid] = pj;
+  }
 }
 
-// Request b, left to right: z_j = logit_j + table_k[prev][j] (prev = row 0 at k = 0), token =
-// the best candidate. The tables of kWalkBlock positions at a time are staged in LDS, every
-// thread's loads in flight together.
+// Request b, left to right: the token after previous slot prev is the candidate in slot
+// next_k[prev] (prev = row 0 at k = 0), the pick topk_bias made over z_j = logit_j +
+// table_k[prev][j]. One wave: the next-slot lists of kWalkBlock positions at a time are loaded
+// together (lane i holds entry i), and the walk chases them with readlane. The candidates' logits
+// on the path (z of the chosen row) are read from the tables only when asked for.
 constexpr int kWalkBlock = 8;
-constexpr int kWalkLoads = kWalkBlock * kMaxCand * kMaxCand / 4 / kThreads;  // float4 per thread
 
-__global__ __launch_bounds__(kThreads) void topk_walk(const int32_t* __restrict__ cand,
-                                                      const float* __restrict__ cand_val,
-                                                      const float* __restrict__ table, int K,
-                                                      int kc, int32_t* __restrict__ tokens,
-                                                      float* __restrict__ cand_logits) {
-  __shared__ __attribute__((aligned(16))) float st[kWalkBlock][kMaxCand][kMaxCand];
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+__global__ __launch_bounds__(64) void topk_walk(const int32_t* __restrict__ cand,
+                                                const float* __restrict__ cand_val,
+                                                const float* __restrict__ table,
+                                                const int32_t* __restrict__ next, int K, int kc,
+                                                int32_t* __restrict__ tokens,
+                                                float* __restrict__ cand_logits) {
+  const int b = blockIdx.x, lane = threadIdx.x & 63;
   int prev = 0;  // slot of the previous token among the previous position's candidates
   for (int k0 = 0; k0 < K; k0 += kWalkBlock) {
     const int nk = K - k0 < kWalkBlock ? K - k0 : kWalkBlock;
-    const int n4 = nk * kMaxCand * kMaxCand / 4;
-    const float4* src = reinterpret_cast<const float4*>(
-        table + ((size_t)b * K + k0) * kMaxCand * kMaxCand);
-    // wave 0's lanes also hold the candidates and logits of the block's positions
-    float val[kWalkBlock];
+    int nx[kWalkBlock];
     int32_t idx[kWalkBlock];
 #pragma unroll
     for (int kk = 0; kk < kWalkBlock; ++kk) {
       const size_t rk = ((size_t)b * K + k0 + (kk < nk ? kk : 0)) * kMaxCand + lane;
-      val[kk] = cand_val[rk];
+      nx[kk] = next[rk];
       idx[kk] = cand[rk];
     }
-    __syncthreads();  // the previous block's tables are read
-    float4* dst = reinterpret_cast<float4*>(&st[0][0][0]);
-    for (int u0 = 0; u0 < kWalkLoads; u0 += 16) {  // sixteen loads in flight per thread
-      float4 buf[16];
+    int rows[kWalkBlock];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int i = (u0 + u) * kThreads + tid;
-        buf[u] = src[i < n4 ? i : 0];
+    for (int kk = 0; kk < kWalkBlock; ++kk) {
+      if (kk < nk) {  // uniform
+        const int k = k0 + kk;
+        const int row = k == 0 ? 0 : prev;
+        rows[kk] = row;
+        prev = __builtin_amdgcn_readlane(nx[kk], row);
+        const int tok = __builtin_amdgcn_readlane(idx[kk], prev);
+        if (lane == 0) tokens[(size_t)b * K + k] = tok;
       }
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-        if ((u0 + u) * kThreads + tid < n4) dst[(u0 + u) * kThreads + tid] = buf[u];
     }
-    __syncthreads();
-    if (tid < 64) {
+    if (cand_logits != nullptr && lane < kc) {
+      float z[kWalkBlock];
 #pragma unroll
       for (int kk = 0; kk < kWalkBlock; ++kk) {
-        if (kk < nk) {  // uniform
-          const int k = k0 + kk;
-          const int row = k == 0 ? 0 : prev;
-          float z = -INFINITY;
-          if (lane < kc) z = val[kk] + st[kk][row][lane];
-          if (cand_logits != nullptr && lane < kc)
-            cand_logits[((size_t)b * K + k) * kc + lane] = z;
-          // argmax over the lanes: the largest z (NaN never wins), then the lowest slot, which
-          // is the lowest vocabulary index
-          const float zz = (lane < kc && z == z) ? z : -INFINITY;
-          const float m = wave_max(zz);
-          prev = (int)__builtin_ctzll(__ballot(zz == m));
-          const int tok = __builtin_amdgcn_readlane(idx[kk], prev);
-          if (lane == 0) tokens[(size_t)b * K + k] = tok;
-        }
+        const size_t rk = (size_t)b * K + k0 + (kk < nk ? kk : 0);
+        z[kk] = cand_val[rk * kMaxCand + lane] +
+                table[(rk * kMaxCand + (kk < nk ? rows[kk] : 0)) * kMaxCand + lane];
       }
+#pragma unroll
+      for (int kk = 0; kk < kWalkBlock; ++kk)
+        if (kk < nk) cand_logits[((size_t)b * K + k0 + kk) * kc + lane] = z[kk];
     }
   }
 }
@@ -653,7 +697,7 @@ bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0;
 int chunks_of(int V) { return (V + kChunk - 1) / kChunk; }
 
 struct TopkWorkspace {
-  size_t chunks, thr, flag, cand, val, table, total;
+  size_t chunks, thr, flag, cand, val, table, next, total;
 };
 
 TopkWorkspace topk_layout(int B, int K, int V) {
@@ -666,7 +710,8 @@ TopkWorkspace topk_layout(int B, int K, int V) {
   w.cand = up(w.flag + rows * chunks_of(V) * sizeof(int32_t));
   w.val = up(w.cand + rows * kMaxCand * sizeof(int32_t));
   w.table = up(w.val + rows * kMaxCand * sizeof(float));
-  w.total = up(w.table + rows * kMaxCand * kMaxCand * sizeof(float));
+  w.next = up(w.table + rows * kMaxCand * kMaxCand * sizeof(float));
+  w.total = up(w.next + rows * kMaxCand * sizeof(int32_t));
   return w;
 }
 
@@ -709,6 +754,7 @@ extern "C" int sv_markov_topk(const void* base_logits, int dtype, int B, int K, 
   int32_t* cand = reinterpret_cast<int32_t*>(ws + w.cand);
   float* val = reinterpret_cast<float*>(ws + w.val);
   float* table = reinterpret_cast<float*>(ws + w.table);
+  int32_t* next = reinterpret_cast<int32_t*>(ws + w.next);
   const int nchunk = chunks_of(V), rows = B * K;
   const size_t es = dtype == SV_DTYPE_F32 ? 4 : 2;
   const bool vec = aligned16(base_logits) && ((size_t)V * es) % 16 == 0;
@@ -733,8 +779,8 @@ extern "C" int sv_markov_topk(const void* base_logits, int dtype, int B, int K, 
   }
   hipLaunchKernelGGL(topk_bias, dim3(rows), dim3(kThreads), 0, s, chunks, thr, nchunk, K, V, kc,
                      dtype == SV_DTYPE_BF16 ? 16 : 0,
-                     left_factor, right_factor, R, anchor, cand, val, candidates, table);
-  hipLaunchKernelGGL(topk_walk, dim3(B), dim3(kThreads), 0, s, cand, val, table, K, kc,
+                     left_factor, right_factor, R, anchor, cand, val, candidates, table, next);
+  hipLaunchKernelGGL(topk_walk, dim3(B), dim3(64), 0, s, cand, val, table, next, K, kc,
                      draft_tokens, cand_logits);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return sv_internal_fail(SV_ERR_HIP, hipGetErrorString(e));
