@@ -15,8 +15,10 @@
 //                table M_k[i][j] = L[cand_{k-1}[i]] . Rf[cand_k[j]] on MFMA (for k = 0 the one
 //                row of the anchor). The token chosen at k-1 is one of cand_{k-1}, so this table
 //                holds every bias position k can need, and no position waits for the one before.
-//   topk_walk    one work-group per request: left to right, z_j = logit_j + M_k[prev][j], the
-//                token is the best candidate (the lowest index on ties), prev its slot.
+//                For every row i of the table it also takes the pick after a previous token in
+//                slot i: the best z_j = logit_j + M_k[i][j] (the lowest index on ties).
+//   topk_walk    one wave per request: left to right, the slot after prev is row prev's pick,
+//                the token is that slot's candidate.
 //
 // Selection keys are the logits' bits mapped to an unsigned order (NaN lowest); a selection
 // keeps the kc largest keys, ties to the earlier entry. A thread owns a contiguous run of
