@@ -143,7 +143,7 @@ Layout make_layout(int B, int K, int V, const Plan& p) {
   Layout L;
   size_t off = 0;
   L.stats = off;
-  off = align_up(off + 16 * (size_t)B * (2 * K + 1) * p.C, 256);
+  off = align_up(off + 16 * (size_t)B * (2 * K + 1) * (p.C + 1), 256);  // a launch may add a chunk
   L.gath = off;
   off = align_up(off + 8 * (size_t)B * 2 * K, 256);
   L.ctot = off;
@@ -578,6 +578,7 @@ struct SampleArgs {
   float c32;  // log2(e) / temperature, rounded to fp32
   int C, C2, NT;
   int L;               // draw groups of request b follow the rows of request b + L (grid order)
+  int CS;              // chunk stride in groups (whole rounds), or 0: an even split
   uint32_t tag;        // this call's tag
   uint64_t* stats;
   uint64_t* gath;  // [B][K][2]
@@ -744,7 +745,13 @@ __device__ __forceinline__ void stream_segments(const T* __restrict__ row, int g
 
 // Chunk c of C of a row of G groups: [G c / C, G (c + 1) / C), with both ends rounded down to a
 // multiple of `align` (a power of two; the last chunk ends at G).
-__device__ __forceinline__ void chunk_bounds(int G, int c, int C, int align, int& g0, int& g1) {
+__device__ __forceinline__ void chunk_bounds(int G, int c, int C, int CS, int align, int& g0,
+                                             int& g1) {
+  if (CS > 0) {  // chunks of CS groups (a multiple of every alignment), the last one shorter
+    g0 = c * CS < G ? c * CS : G;
+    g1 = c + 1 == C ? G : ((c + 1) * CS < G ? (c + 1) * CS : G);
+    return;
+  }
   g0 = (int)((long)G * c / C) & ~(align - 1);
   g1 = c + 1 == C ? G : (int)((long)G * (c + 1) / C) & ~(align - 1);
 }
@@ -765,7 +772,7 @@ __device__ void row_stat_group(const SampleArgs& a, int b, int slot, int c) {
   const int G = VEC ? V / E : V;
   const bool bonus = slot == k && a.NS > 0;  // the row of p_k, streamed in segments
   int g0, g1;
-  chunk_bounds(G, c, C, bonus ? kSegGroups : 1, g0, g1);
+  chunk_bounds(G, c, C, a.CS, bonus ? kSegGroups : 1, g0, g1);
   if (GEN && q.greedy) {  // greedy request: argmax partials of target rows 0..k, no draft rows
     if (slot > k) return;
     argmax_chunk<T, VEC>(q.t0 + (size_t)slot * V, g0, g1,
@@ -1894,6 +1901,26 @@ int launch_sample(const SampleArgs& args, hipStream_t stream) {
   if (VEC && sizeof(T) == 2 && a.C > kBf16Chunks) a.C = kBf16Chunks;
   if (VEC && sizeof(T) == 4 && a.C > kF32Chunks && (long)a.B * (2 * a.K + 1) * kF32Chunks >= 1024)
     a.C = kF32Chunks;
+  // Chunks of whole rounds: when an even split leaves each chunk a few groups past a whole number
+  // of rounds (kUnroll loads per thread), those few go through the one-group tail, one more memory
+  // round trip in every chunk; one more chunk (the workspace has room for it), all the others of
+  // whole rounds and the last one shorter, avoids it. (B = 1, float32, V = 151936: 37 chunks of
+  // 1027 groups became 38 of 1024.)
+  a.CS = 0;
+  {
+    const long E = VEC ? 16 / (long)sizeof(T) : 1;
+    const long G = VEC ? a.V / E : a.V;
+    const long R = (long)kUnroll * kBlock;
+    const long S = (G + a.C - 1) / a.C;
+    const long m = S / R;
+    if (m >= 1 && S - m * R <= R / 16) {
+      const long C1 = (G + m * R - 1) / (m * R);
+      if (C1 <= args.C + 1 && (2L * a.K + 1) * C1 <= kStageMax) {
+        a.C = (int)C1;
+        a.CS = (int)(m * R);
+      }
+    }
+  }
   // The lag: about the number of requests whose row-stat groups are resident at once, plus two.
   // In ragged batches (verify lengths per request) the rows past k_b are skipped, so the host
   // cannot tell how many requests stream at once; a lag too short makes draw groups wait for
