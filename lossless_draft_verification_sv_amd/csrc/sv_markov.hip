@@ -87,7 +87,8 @@ __device__ __forceinline__ bool better(float z, int i, float best, int bi) {
 constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
 template <int CTRL>
 __device__ __forceinline__ float dpp_xchg_f32(float x) {
-  return __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)__float_as_uint(x), CTRL, 0xf, 0xf, false));
+  return __uint_as_float(
+      (uint32_t)__builtin_amdgcn_mov_dpp((int)__float_as_uint(x), CTRL, 0xf, 0xf, false));
 }
 template <int CTRL>
 __device__ __forceinline__ void argmax_step(float& best, int& bi) {
@@ -224,8 +225,8 @@ __global__ __launch_bounds__(kThreads) void markov_bias_tile(
       bi = tile * kTileV + col;
     }
   }
-argmax_step<kDppXor1>(best, bi);
-argmax_step<kDppXor2>(best, bi);
+  argmax_step<kDppXor1>(best, bi);
+  argmax_step<kDppXor2>(best, bi);
   const int b = b0 + m;
   if (q == 0 && b < B)
     part[(size_t)b * ntile + tile] = ((uint64_t)__float_as_uint(best) << 32) | (uint32_t)bi;
@@ -463,8 +464,8 @@ __device__ __forceinline__ void stream_item(const StreamArgs& a, const T* __rest
           if (e < ncol) Logit<T>::put(orow + e, z[e]);
       }
     }
-argmax_step<kDppXor1>(best, bi);
-argmax_step<kDppXor2>(best, bi);
+    argmax_step<kDppXor1>(best, bi);
+    argmax_step<kDppXor2>(best, bi);
   }
   if (q == 0 && b < a.B)
     a.part[(size_t)b * a.ntile + tile] = ((uint64_t)__float_as_uint(best) << 32) | (uint32_t)bi;
@@ -706,8 +707,8 @@ __device__ __forceinline__ void res_tile(const ResArgs& a, T* __restrict__ out,
           if (e < ncol) Logit<T>::put(orow + e, z[e]);
       }
     }
-argmax_step<kDppXor1>(best, bi);
-argmax_step<kDppXor2>(best, bi);
+    argmax_step<kDppXor1>(best, bi);
+    argmax_step<kDppXor2>(best, bi);
     if (better(best, bi, run, run_i)) {
       run = best;
       run_i = bi;
@@ -1119,7 +1120,7 @@ markov_resident(const T* __restrict__ base, T* __restrict__ out, ResArgs a) {
           }
         }
       }
-wave_argmax(best, bi);
+      wave_argmax(best, bi);
       const bool wave_late = __ballot(late) != 0;
       if (lane == 0) {
         s_best[wave] = best;
@@ -1332,9 +1333,9 @@ __device__ __forceinline__ void pipe_tile(const ResArgs& a, T* __restrict__ out,
           if (e < ncol) Logit<T>::put(orow + e, z[e]);
       }
     }
-argmax_step<kDppXor1>(best, bi);
-argmax_step<kDppXor2>(best, bi);
-argmax_step<kDppHalfMirror>(best, bi);
+    argmax_step<kDppXor1>(best, bi);
+    argmax_step<kDppXor2>(best, bi);
+    argmax_step<kDppHalfMirror>(best, bi);
     if (better(best, bi, run, run_i)) {
       run = best;
       run_i = bi;
@@ -1449,7 +1450,7 @@ markov_pipe(const T* __restrict__ base, T* __restrict__ out, ResArgs a) {
           }
         }
       }
-wave_argmax(best, bi);
+      wave_argmax(best, bi);
       const bool wave_late = __ballot(late) != 0;
       if (lane == 0) {
         s_best[wave] = best;

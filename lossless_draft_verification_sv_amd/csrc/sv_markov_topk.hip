@@ -105,7 +105,8 @@ __device__ __forceinline__ bool pick_better(float z, int i, float best, int bi) 
 template <int CTRL>
 __device__ __forceinline__ void pick_step(float& best, int& bi) {
   const float b2 =
-      __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)__float_as_uint(best), CTRL, 0xf, 0xf, false));
+      __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)__float_as_uint(best), CTRL, 0xf,
+                                                          0xf, false));
   const int i2 = __builtin_amdgcn_mov_dpp(bi, CTRL, 0xf, 0xf, false);
   if (pick_better(b2, i2, best, bi)) {
     best = b2;
