@@ -219,6 +219,16 @@ def test_full_interactive_B1_K8_f32():
     _check(generate(INTERACTIVE))
 
 
+def test_full_vocabulary_f32_chunks_of_whole_rounds():
+    """Float32 rows of the Qwen3 vocabulary at B = 4: an even split into the plan's 37 chunks
+    leaves each a round and a three-group tail, so the launch cuts 38 chunks of whole rounds, the
+    last one shorter (the bonus rows' segments among them); half the requests keep every draft."""
+    w = INTERACTIVE.replace(name="whole_rounds_B4_K8_V151936_f32", B=4, identical_even=True,
+                            seed=3701)
+    s = _check(generate(w))
+    assert s["requests"] == 4
+
+
 def test_full_batched_B64_K8_bf16():
     s = _check(generate(BATCHED))
     assert s["requests"] == 64
