@@ -172,7 +172,9 @@ def test_markov_zero_factors_is_per_position_argmax():
     B, K, V = 17, 6, 2000
     base = workloads.markov_base(B, K, V, "bf16", seed=24)
     base[:, :, 5] = base[:, :, 7] = workloads.to_bf16_bits(np.array([50.0], np.float32))[0]
-    vals_t = workloads.bf16_bits_to_f32(base)  # 50 at 5 and at 7: the lowest index wins
+    # the same maximum in other lanes, tiles and work-groups: the lowest index still wins
+    base[:, :, 700] = base[:, :, 1999] = base[:, :, 5]
+    vals_t = workloads.bf16_bits_to_f32(base)  # 50 at 5, 7, 700 and 1999: the lowest index wins
     zero = np.zeros((V, 32), np.uint16)
     tok, logits = run(base, zero, zero, np.arange(B, dtype=np.int32))
     assert np.all(tok == 5)
