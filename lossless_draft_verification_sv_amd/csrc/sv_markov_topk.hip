@@ -42,7 +42,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxCand = 64;                 // kc limit: one MFMA-tiled 64 x 64 bias table
-constexpr int kPerThread = 64;               // entries a thread selects over
+constexpr int kPerThread = 128;               // entries a thread selects over
 constexpr int kChunk = kThreads * kPerThread;  // logits per chunk work-group
 constexpr int kCompact = 1024;               // chunk entries above the first bound kept in LDS
 constexpr int kExactPer = 16;                // chunks one exact-pass work-group looks at
