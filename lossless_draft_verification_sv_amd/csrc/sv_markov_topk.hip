@@ -430,8 +430,9 @@ __global__ __launch_bounds__(kThreads) void topk_chunk(const T* __restrict__ bas
   }
   __syncthreads();
   uint64_t* dst = out + ((size_t)r * nchunk + c) * kMaxCand;
-  if (wave == 0) {
+  if (wave == 0) {  // the two selections read the list only: one wave each, side by side
     list_select<4>(sh, n_all, kc, kLow, [&](int slot, uint64_t e) { dst[slot] = e; });
+  } else if (wave == 1) {
     const uint32_t t = list_kth<4>(sh, n_all, q_thr, kLow);
     if (lane == 0) thr[(size_t)r * nchunk + c] = t;
   }
